@@ -1,0 +1,189 @@
+/*
+ * libdgfp8 -- FP8 GEMM with fine-grained block scaling for MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every pointer marked "device" is a
+ * device address on the current HIP device; "stream" is a hipStream_t passed
+ * as void* (NULL selects the default stream).  All work is enqueued on that
+ * stream and the call returns without synchronising.  The caller owns every
+ * buffer; the library allocates nothing per call and keeps no device state
+ * besides the compute-unit count used for the persistent grid.
+ *
+ * Errors: every entry point validates its arguments on the host and returns a
+ * dg_status.  Nothing aborts and no exception crosses the ABI.  A problem
+ * with a zero-sized dimension returns DG_SUCCESS without launching anything.
+ * Device-side preconditions that are not checked are stated per function.
+ *
+ * Method (pages on DeepGEMM): D(bf16) = A . B^T in the NT layout (both
+ * operands K-major), with E4M3 A carrying one fp32 scale per row per 128-wide
+ * K block and E4M3 B one fp32 scale per 128x128 block; every K block's partial
+ * product is scaled and promoted into an fp32 accumulator.  Sources: page
+ * "GitHub 推荐：DeepSeek 开源周最大黑马 DeepGEMM…" (问题判断: 128x128 block
+ * scaling; 创新之处: per-block scaling through promotion; 解法哲学: the
+ * fp8_gemm_nt call with a caller-provided output d); page juejin.cn post on
+ * DeepGEMM (section 3: two-level accumulation and M-only grouping; section
+ * 4(3): dense, contiguous and masked GEMM types; section 5: API names).
+ *
+ * Scale-factor contract (all GEMM entry points):
+ *   SFA is fp32, logically [rows, K/128]; element (i, kb) lives at
+ *       sfa[i * sfa_sm + kb * sfa_sk]  (row-major: sfa_sm = K/128, sfa_sk = 1;
+ *       MN-major / "transposed": sfa_sm = 1, sfa_sk = rows).
+ *   SFB is fp32, logically [ceil(N/128), K/128]; element (nb, kb) at
+ *       sfb[nb * sfb_sn + kb * sfb_sk]; output column j uses nb = j / 128.
+ *   E4M3 is the OCP "FN" flavour (largest finite 448, no infinities).
+ *   Strides are in elements and must be >= 0.
+ *
+ * Alignment contract: K % 128 == 0; lda, ldb and the A/B base addresses are
+ * multiples of 16 bytes; N % 8 == 0, ldd % 8 == 0 and D is 16-byte aligned.
+ * Violations return DG_ERROR_NOT_SUPPORTED.
+ */
+#ifndef DGFP8_H_
+#define DGFP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_SUCCESS = 0,
+  DG_ERROR_INVALID_VALUE = 1,     /* null pointer, negative size, bad stride, bad group count */
+  DG_ERROR_NOT_SUPPORTED = 2,     /* K % 128 != 0, misaligned pointer / leading dimension, N % 8 != 0 */
+  DG_ERROR_MISALIGNED_LAYOUT = 3, /* contiguous layout: m_total % 128 != 0 */
+  DG_ERROR_LAUNCH = 4             /* HIP reported an error at launch */
+} dg_status;
+
+/* Human-readable name of a status; never NULL. */
+const char* dg_status_string(dg_status status);
+
+/*
+ * Dense GEMM: D[m, n] = sum_kb sfa[m, kb] * sfb[n/128, kb] * sum_{k in kb} A[m, k] * B[n, k],
+ * rounded to bf16 (round to nearest even).
+ *   a   device, E4M3 [m, k], row stride lda (bytes = elements)
+ *   sfa device, fp32, see the scale-factor contract (rows = m)
+ *   b   device, E4M3 [n, k], row stride ldb
+ *   sfb device, fp32 [ceil(n/128), k/128] with strides sfb_sn, sfb_sk
+ *   d   device, bf16 [m, n], row stride ldd (elements); fully overwritten
+ * Page "GitHub 推荐…DeepGEMM…", 解法哲学 (fp8_gemm_nt with output d);
+ * page juejin.cn, section 4(3) (dense GEMM type).
+ */
+dg_status dg_fp8_gemm_nt(const void* a, int64_t lda,
+                         const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                         const void* b, int64_t ldb,
+                         const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                         void* d, int64_t ldd,
+                         int64_t m, int64_t n, int64_t k,
+                         void* stream);
+
+/*
+ * M-grouped GEMM, contiguous layout (MoE prefill / training forward).
+ * The rows of all groups are concatenated along M; each group's segment is
+ * padded to a multiple of 128 rows (dg_get_mk_alignment_for_contiguous_layout).
+ *   a         device, E4M3 [m_total, k], row stride lda
+ *   sfa       device, fp32, rows = m_total (scale-factor contract)
+ *   b         device, E4M3 [num_groups, n, k]; group g starts at b + g * b_group_stride,
+ *             rows of a group have stride ldb
+ *   sfb       device, fp32 [num_groups, ceil(n/128), k/128]; group g at sfb + g * sfb_group_stride
+ *   d         device, bf16 [m_total, n], row stride ldd
+ *   m_indices device, int32 [m_total]: group of each row, -1 on padding rows
+ * Row i with m_indices[i] = g >= 0 gets row i of A times B[g]^T.  Rows with
+ * m_indices[i] == -1 are NOT written (their contents are left untouched).
+ * Preconditions (not checked on the device): in each aligned 128-row block
+ * every row with m_indices >= 0 has the same value, which lies in
+ * [0, num_groups).  The group of a block is read from its first row; a block
+ * whose first row is -1 is skipped entirely.
+ * Errors: m_total % 128 != 0 -> DG_ERROR_MISALIGNED_LAYOUT.
+ * Page juejin.cn, sections 3 and 4(3) (M-only grouping, contiguous layout
+ * aligned to the M block); page "GitHub 推荐…", 风险与不足 (128-row padding).
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, int64_t lda,
+                                              const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                              const void* b, int64_t ldb, int64_t b_group_stride,
+                                              const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                              int64_t sfb_group_stride,
+                                              void* d, int64_t ldd,
+                                              const int32_t* m_indices, int64_t m_total,
+                                              int64_t n, int64_t k, int num_groups,
+                                              void* stream);
+
+/*
+ * M-grouped GEMM, masked layout (MoE decode; usable under HIP graph capture).
+ *   a        device, E4M3 [num_groups, max_m, k]; group g at a + g * a_group_stride, rows lda
+ *   sfa      device, fp32 [num_groups, max_m, k/128]; group g at sfa + g * sfa_group_stride,
+ *            then the scale-factor contract with rows = max_m
+ *   b, sfb   as in the contiguous variant
+ *   d        device, bf16 [num_groups, max_m, n]; group g at d + g * d_group_stride, rows ldd
+ *   masked_m device, int32 [num_groups]: valid rows of each group, read on the
+ *            device at run time (never by the host), clamped to [0, max_m]
+ *   expected_m  hint of the typical masked_m; never changes results
+ * For group g, rows i < masked_m[g] get A[g, i] times B[g]^T; rows at or beyond
+ * masked_m[g] are left untouched.
+ * Page juejin.cn, section 4(3) (masked grouped GEMM for decode with graphs).
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, int64_t lda, int64_t a_group_stride,
+                                          const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                          int64_t sfa_group_stride,
+                                          const void* b, int64_t ldb, int64_t b_group_stride,
+                                          const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                          int64_t sfb_group_stride,
+                                          void* d, int64_t ldd, int64_t d_group_stride,
+                                          const int32_t* masked_m, int num_groups,
+                                          int64_t max_m, int64_t n, int64_t k,
+                                          int64_t expected_m,
+                                          void* stream);
+
+/*
+ * Per-token FP8 cast (the library's GEMMs take E4M3 inputs; the caller does the
+ * cast: page ssnai.com DeepGEMM analysis, the warning that casting is the
+ * caller's job).  For each row i and 128-wide block kb of a bf16 [m, k] input:
+ *   amax = max |x|;  s = fl32(max(amax, 1e-4) / 448)  (IEEE fp32 division);
+ *   if ue8m0 != 0: s = smallest power of two >= s;
+ *   q = E4M3 round-to-nearest-even of clamp(fl32(x / s), -448, 448), sign kept.
+ *   x   device, bf16 [m, k], row stride ldx (elements), 16-byte aligned rows
+ *   q   device, E4M3 [m, k], row stride ldq (bytes), 16-byte aligned rows
+ *   sf  device, fp32 [m, k/128]: element (i, kb) at sf[i * sf_sm + kb * sf_sk]
+ * Results are bit-exact with the definition above.
+ */
+dg_status dg_per_token_cast_fp8(const void* x, int64_t ldx,
+                                void* q, int64_t ldq,
+                                float* sf, int64_t sf_sm, int64_t sf_sk,
+                                int64_t m, int64_t k, int ue8m0,
+                                void* stream);
+
+/* Same as dg_per_token_cast_fp8 for an fp32 [m, k] input. */
+dg_status dg_per_token_cast_fp8_f32(const void* x, int64_t ldx,
+                                    void* q, int64_t ldq,
+                                    float* sf, int64_t sf_sm, int64_t sf_sk,
+                                    int64_t m, int64_t k, int ue8m0,
+                                    void* stream);
+
+/*
+ * Weight-side cast: fp32 [n, k] -> E4M3 [n, k] with one scale per 128x128 block
+ * (rows beyond n in the last block do not exist and do not enter its amax).
+ * Same scale and code rules as dg_per_token_cast_fp8, amax taken over the block.
+ *   sf  device, fp32 [ceil(n/128), k/128]: element (nb, kb) at sf[nb * sf_sn + kb * sf_sk]
+ */
+dg_status dg_per_block_cast_fp8(const void* x, int64_t ldx,
+                                void* q, int64_t ldq,
+                                float* sf, int64_t sf_sn, int64_t sf_sk,
+                                int64_t n, int64_t k, int ue8m0,
+                                void* stream);
+
+/* Row alignment of each group's segment in the contiguous layout: 128.
+ * (Page ssnai.com DeepGEMM analysis: the alignment query for contiguous MoE.) */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/*
+ * Width of the persistent GEMM grid in compute units (default: all CUs of the
+ * current device).  Results never depend on it.  num_cus <= 0 restores the
+ * default.  (Analog of set_num_sms: page ssnai.com DeepGEMM analysis.)
+ */
+dg_status dg_set_num_cus(int num_cus);
+int dg_get_num_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGFP8_H_ */

@@ -1,0 +1,205 @@
+"""Python binding of libdgfp8: FP8 block-scaled GEMMs and FP8 casts for MI355X.
+
+Argument marshalling only.  Each function checks dtypes/devices, hands raw
+device pointers, strides and torch's current HIP stream to the C ABI declared
+in ``include/dgfp8.h`` and raises ``DgError`` on a non-zero status.  All
+arithmetic runs in the HIP kernels of ``libdgfp8.so``; there is no fallback:
+importing this package fails loudly when the library has not been built.
+
+Tensor conventions (torch): E4M3 operands are ``torch.float8_e4m3fn`` (or
+``torch.uint8`` holding the codes), scales ``torch.float32`` with any
+non-negative strides, outputs ``torch.bfloat16``.  Operands and scales are
+passed as pairs ``(codes, scales)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdgfp8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_fp8_gemm_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+
+_SIGNATURES = {
+    "dg_status_string": ([_i32], ctypes.c_char_p),
+    "dg_fp8_gemm_nt": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
+                        _i64, _i64, _i64, _p], _i32),
+    "dg_m_grouped_fp8_gemm_nt_contiguous": ([_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64,
+                                             _p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
+    "dg_m_grouped_fp8_gemm_nt_masked": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                         _i64, _p, _i64, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p], _i32),
+    "dg_per_token_cast_fp8": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _i32, _p], _i32),
+    "dg_per_token_cast_fp8_f32": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _i32, _p], _i32),
+    "dg_per_block_cast_fp8": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _i32, _p], _i32),
+    "dg_get_mk_alignment_for_contiguous_layout": ([], _i32),
+    "dg_set_num_cus": ([_i32], _i32),
+    "dg_get_num_cus": ([], _i32),
+}
+for _name, (_args, _res) in _SIGNATURES.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+DG_SUCCESS = 0
+DG_ERROR_INVALID_VALUE = 1
+DG_ERROR_NOT_SUPPORTED = 2
+DG_ERROR_MISALIGNED_LAYOUT = 3
+DG_ERROR_LAUNCH = 4
+
+
+class DgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.dg_status_string(status).decode()}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != DG_SUCCESS:
+        raise DgError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} must be float8_e4m3fn or uint8 codes, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must be K-major (unit stride along K)")
+    return t
+
+
+def _scales(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 device tensor")
+    return t
+
+
+def _out_bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16 or not t.is_cuda or t.stride(-1) != 1:
+        raise TypeError(f"{name} must be a bfloat16 device tensor with unit column stride")
+    return t
+
+
+def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
+                d: torch.Tensor) -> torch.Tensor:
+    """d[m, n] = bf16( A . B^T ) with per-(row, 128-K) A scales and per-128x128 B scales.
+
+    a = (codes [m, k], sfa [m, k/128]); b = (codes [n, k], sfb [ceil(n/128), k/128]);
+    d bf16 [m, n] is overwritten and returned.
+    """
+    (qa, sa), (qb, sb) = a, b
+    _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
+    m, k = qa.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k or d.shape != (m, n):
+        raise ValueError("shape mismatch")
+    _check(lib.dg_fp8_gemm_nt(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+                              qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
+                              d.data_ptr(), d.stride(0), m, n, k, _stream()), "dg_fp8_gemm_nt")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
+    """Contiguous MoE layout: a = (codes [m_total, k], sfa [m_total, k/128]),
+    b = (codes [G, n, k], sfb [G, ceil(n/128), k/128]), d bf16 [m_total, n],
+    m_indices int32 [m_total] (-1 on padding rows, which are left untouched)."""
+    (qa, sa), (qb, sb) = a, b
+    _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
+    if m_indices.dtype != torch.int32 or not m_indices.is_cuda:
+        raise TypeError("m_indices must be an int32 device tensor")
+    m_total, k = qa.shape
+    g, n, _ = qb.shape
+    if qb.shape[2] != k or d.shape != (m_total, n) or m_indices.shape != (m_total,) or m_indices.stride(0) != 1:
+        raise ValueError("shape mismatch")
+    _check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(
+        qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+        qb.data_ptr(), qb.stride(1), qb.stride(0),
+        sb.data_ptr(), sb.stride(1), sb.stride(2), sb.stride(0),
+        d.data_ptr(), d.stride(0), m_indices.data_ptr(), m_total, n, k, g, _stream()),
+        "dg_m_grouped_fp8_gemm_nt_contiguous")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor,
+                                 expected_m: int) -> torch.Tensor:
+    """Masked MoE layout: a = (codes [G, max_m, k], sfa [G, max_m, k/128]),
+    b = (codes [G, n, k], sfb [G, ceil(n/128), k/128]), d bf16 [G, max_m, n],
+    masked_m int32 [G] read on the device; rows >= masked_m[g] are left untouched."""
+    (qa, sa), (qb, sb) = a, b
+    _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
+    if masked_m.dtype != torch.int32 or not masked_m.is_cuda:
+        raise TypeError("masked_m must be an int32 device tensor")
+    g, max_m, k = qa.shape
+    n = qb.shape[1]
+    if qb.shape != (g, n, k) or d.shape != (g, max_m, n) or masked_m.shape != (g,):
+        raise ValueError("shape mismatch")
+    _check(lib.dg_m_grouped_fp8_gemm_nt_masked(
+        qa.data_ptr(), qa.stride(1), qa.stride(0),
+        sa.data_ptr(), sa.stride(1), sa.stride(2), sa.stride(0),
+        qb.data_ptr(), qb.stride(1), qb.stride(0),
+        sb.data_ptr(), sb.stride(1), sb.stride(2), sb.stride(0),
+        d.data_ptr(), d.stride(1), d.stride(0),
+        masked_m.data_ptr(), g, max_m, n, k, int(expected_m), _stream()),
+        "dg_m_grouped_fp8_gemm_nt_masked")
+    return d
+
+
+def _cast_out(rows: int, k: int, device, q: Optional[torch.Tensor], sf: Optional[torch.Tensor], sf_rows: int):
+    if q is None:
+        q = torch.empty((rows, k), dtype=torch.float8_e4m3fn, device=device)
+    if sf is None:
+        sf = torch.empty((sf_rows, k // 128), dtype=torch.float32, device=device)
+    return q, sf
+
+
+def per_token_cast_fp8(x: torch.Tensor, ue8m0: bool = False, q: Optional[torch.Tensor] = None,
+                       sf: Optional[torch.Tensor] = None):
+    """x bf16 or fp32 [m, k] -> (E4M3 codes [m, k], fp32 scales [m, k/128]), 1x128 blocks."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_cuda or x.stride(-1) != 1:
+        raise TypeError("x must be a bf16 or fp32 device tensor with unit column stride")
+    m, k = x.shape
+    q, sf = _cast_out(m, k, x.device, q, sf, m)
+    fn = lib.dg_per_token_cast_fp8_f32 if x.dtype == torch.float32 else lib.dg_per_token_cast_fp8
+    _check(fn(x.data_ptr(), x.stride(0), q.data_ptr(), q.stride(0), sf.data_ptr(), sf.stride(0), sf.stride(1),
+              m, k, int(bool(ue8m0)), _stream()), "per_token_cast_fp8")
+    return q, sf
+
+
+def per_block_cast_fp8(w: torch.Tensor, ue8m0: bool = False, q: Optional[torch.Tensor] = None,
+                       sf: Optional[torch.Tensor] = None):
+    """w fp32 [n, k] -> (E4M3 codes [n, k], fp32 scales [ceil(n/128), k/128]), 128x128 blocks."""
+    if w.dtype != torch.float32 or not w.is_cuda or w.stride(-1) != 1:
+        raise TypeError("w must be an fp32 device tensor with unit column stride")
+    n, k = w.shape
+    q, sf = _cast_out(n, k, w.device, q, sf, (n + 127) // 128)
+    _check(lib.dg_per_block_cast_fp8(w.data_ptr(), w.stride(0), q.data_ptr(), q.stride(0), sf.data_ptr(),
+                                     sf.stride(0), sf.stride(1), n, k, int(bool(ue8m0)), _stream()),
+           "per_block_cast_fp8")
+    return q, sf
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return lib.dg_get_mk_alignment_for_contiguous_layout()
+
+
+def set_num_cus(num_cus: int) -> None:
+    _check(lib.dg_set_num_cus(int(num_cus)), "dg_set_num_cus")
+
+
+def get_num_cus() -> int:
+    return lib.dg_get_num_cus()

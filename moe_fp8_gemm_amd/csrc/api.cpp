@@ -1,0 +1,223 @@
+// Host side of the C ABI: argument validation (the caller's faults come back as
+// status codes, in the spirit of the host assertions the pages describe: page
+// "GitHub 推荐…DeepGEMM…", 解法哲学 and 可复用的模式与技巧 on layout validation),
+// choice of a compiled kernel instance, and launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "dgfp8_internal.h"
+
+#define DG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace dgfp8 {
+namespace {
+
+constexpr int kContiguousAlignment = 128;
+constexpr int kMaxMaskedGroups = 1024;
+constexpr int kMaxDevices = 64;
+
+int g_num_cus_override = 0;
+int g_device_cus[kMaxDevices] = {0};
+
+int device_cus() {
+  if (g_num_cus_override > 0) return g_num_cus_override;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (g_device_cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_device_cus[dev] = v;
+  }
+  return g_device_cus[dev];
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by the three GEMM variants.
+dg_status check_common(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                       const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                       const void* d, int64_t ldd, int64_t n, int64_t k) {
+  if (!a || !b || !d || !sfa || !sfb) return DG_ERROR_INVALID_VALUE;
+  if (n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
+  if (sfa_sm < 0 || sfa_sk < 0 || sfb_sn < 0 || sfb_sk < 0) return DG_ERROR_INVALID_VALUE;
+  if (lda < k || ldb < k || ldd < n) return DG_ERROR_INVALID_VALUE;
+  if (k == 0 || k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (n % 8 != 0 || ldd % 8 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (lda % 16 != 0 || ldb % 16 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16)) return DG_ERROR_NOT_SUPPORTED;
+  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return DG_ERROR_NOT_SUPPORTED;
+  return DG_SUCCESS;
+}
+
+// Static instance table: the wide 128x256 tile when it already yields at least
+// one tile per CU, else the 128x128 tile for more parallelism.
+GemmInstance choose_instance(int64_t m_tiles_128, int64_t n, int cus) {
+  const int64_t wide_tiles = m_tiles_128 * ((n + 255) / 256);
+  return wide_tiles >= cus ? kInstLarge : kInstMid;
+}
+
+dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile_bound, hipStream_t stream) {
+  const int cus = device_cus();
+  int64_t grid = tile_bound < cus ? tile_bound : cus;
+  if (grid <= 0) return DG_SUCCESS;
+  if (tile_bound > INT_MAX) return DG_ERROR_NOT_SUPPORTED;
+  return launch_gemm(inst, v, p, (int)grid, stream) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+}  // namespace dgfp8
+
+using namespace dgfp8;
+
+DG_EXPORT const char* dg_status_string(dg_status status) {
+  switch (status) {
+    case DG_SUCCESS: return "DG_SUCCESS";
+    case DG_ERROR_INVALID_VALUE: return "DG_ERROR_INVALID_VALUE";
+    case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED";
+    case DG_ERROR_MISALIGNED_LAYOUT: return "DG_ERROR_MISALIGNED_LAYOUT";
+    case DG_ERROR_LAUNCH: return "DG_ERROR_LAUNCH";
+  }
+  return "DG_ERROR_UNKNOWN";
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                   const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                   void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* stream) {
+  if (m < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return DG_SUCCESS;
+  dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
+  if (st != DG_SUCCESS) return st;
+  GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a); p.lda = lda;
+  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
+  p.b = static_cast<const uint8_t*>(b); p.ldb = ldb;
+  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
+  p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1;
+  const GemmInstance inst = choose_instance(ceil_div(m, 128), n, device_cus());
+  const InstanceInfo info = instance_info(inst);
+  const int64_t tiles = ceil_div(m, info.bm) * ceil_div(n, info.bn);
+  return launch(inst, kDense, p, tiles, static_cast<hipStream_t>(stream));
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
+    const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
+    int64_t n, int64_t k, int num_groups, void* stream) {
+  if (m_total < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
+  if (b_group_stride < 0 || sfb_group_stride < 0) return DG_ERROR_INVALID_VALUE;
+  if (m_total % kContiguousAlignment != 0) return DG_ERROR_MISALIGNED_LAYOUT;
+  if (m_total == 0 || n == 0) return DG_SUCCESS;
+  if (!m_indices) return DG_ERROR_INVALID_VALUE;
+  dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
+  if (st != DG_SUCCESS) return st;
+  if (b_group_stride % 16 != 0 || !aligned(m_indices, 4)) return DG_ERROR_NOT_SUPPORTED;
+  GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a); p.lda = lda;
+  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
+  p.b = static_cast<const uint8_t*>(b); p.ldb = ldb; p.b_gs = b_group_stride;
+  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
+  p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
+  p.m_indices = m_indices;
+  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
+  const GemmInstance inst = choose_instance(m_total / 128, n, device_cus());
+  const InstanceInfo info = instance_info(inst);
+  const int64_t tiles = (m_total / info.bm) * ceil_div(n, info.bn);
+  return launch(inst, kContiguous, p, tiles, static_cast<hipStream_t>(stream));
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
+    const void* a, int64_t lda, int64_t a_group_stride,
+    const float* sfa, int64_t sfa_sm, int64_t sfa_sk, int64_t sfa_group_stride,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, int64_t d_group_stride,
+    const int32_t* masked_m, int num_groups, int64_t max_m, int64_t n, int64_t k,
+    int64_t expected_m, void* stream) {
+  (void)expected_m;   // a size hint; results never depend on it
+  if (max_m < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
+  if (a_group_stride < 0 || sfa_group_stride < 0 || b_group_stride < 0 || sfb_group_stride < 0 ||
+      d_group_stride < 0)
+    return DG_ERROR_INVALID_VALUE;
+  if (num_groups > kMaxMaskedGroups) return DG_ERROR_NOT_SUPPORTED;
+  if (max_m == 0 || n == 0) return DG_SUCCESS;
+  if (!masked_m) return DG_ERROR_INVALID_VALUE;
+  dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
+  if (st != DG_SUCCESS) return st;
+  if (a_group_stride % 16 != 0 || b_group_stride % 16 != 0 || d_group_stride % 8 != 0 || !aligned(masked_m, 4))
+    return DG_ERROR_NOT_SUPPORTED;
+  GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a); p.lda = lda; p.a_gs = a_group_stride;
+  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk; p.sfa_gs = sfa_group_stride;
+  p.b = static_cast<const uint8_t*>(b); p.ldb = ldb; p.b_gs = b_group_stride;
+  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
+  p.d = static_cast<uint16_t*>(d); p.ldd = ldd; p.d_gs = d_group_stride;
+  p.masked_m = masked_m;
+  p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
+  const GemmInstance inst = choose_instance((int64_t)num_groups * ceil_div(max_m, 128), n, device_cus());
+  const InstanceInfo info = instance_info(inst);
+  const int64_t bound = (int64_t)num_groups * ceil_div(max_m, info.bm) * ceil_div(n, info.bn);
+  return launch(inst, kMasked, p, bound, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+dg_status cast_checks(const void* x, int64_t ldx, int64_t x_elem, const void* q, int64_t ldq, const float* sf,
+                      int64_t s0, int64_t s1, int64_t rows, int64_t k) {
+  if (rows < 0 || k < 0 || s0 < 0 || s1 < 0) return DG_ERROR_INVALID_VALUE;
+  if (rows == 0 || k == 0) return DG_SUCCESS;
+  if (!x || !q || !sf) return DG_ERROR_INVALID_VALUE;
+  if (ldx < k || ldq < k) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if ((ldx * x_elem) % 16 != 0 || ldq % 16 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return DG_ERROR_NOT_SUPPORTED;
+  return DG_SUCCESS;
+}
+
+dg_status per_token(const void* x, int64_t ldx, void* q, int64_t ldq, float* sf, int64_t sf_sm, int64_t sf_sk,
+                    int64_t m, int64_t k, int ue8m0, bool f32, void* stream) {
+  dg_status st = cast_checks(x, ldx, f32 ? 4 : 2, q, ldq, sf, sf_sm, sf_sk, m, k);
+  if (st != DG_SUCCESS || m == 0 || k == 0) return st;
+  CastParams p{x, ldx, static_cast<uint8_t*>(q), ldq, sf, sf_sm, sf_sk, m, k, ue8m0 ? 1 : 0};
+  return launch_per_token_cast(p, f32, device_cus(), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DG_SUCCESS : DG_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+DG_EXPORT dg_status dg_per_token_cast_fp8(const void* x, int64_t ldx, void* q, int64_t ldq, float* sf,
+                                          int64_t sf_sm, int64_t sf_sk, int64_t m, int64_t k, int ue8m0,
+                                          void* stream) {
+  return per_token(x, ldx, q, ldq, sf, sf_sm, sf_sk, m, k, ue8m0, false, stream);
+}
+
+DG_EXPORT dg_status dg_per_token_cast_fp8_f32(const void* x, int64_t ldx, void* q, int64_t ldq, float* sf,
+                                              int64_t sf_sm, int64_t sf_sk, int64_t m, int64_t k, int ue8m0,
+                                              void* stream) {
+  return per_token(x, ldx, q, ldq, sf, sf_sm, sf_sk, m, k, ue8m0, true, stream);
+}
+
+DG_EXPORT dg_status dg_per_block_cast_fp8(const void* x, int64_t ldx, void* q, int64_t ldq, float* sf,
+                                          int64_t sf_sn, int64_t sf_sk, int64_t n, int64_t k, int ue8m0,
+                                          void* stream) {
+  dg_status st = cast_checks(x, ldx, 4, q, ldq, sf, sf_sn, sf_sk, n, k);
+  if (st != DG_SUCCESS || n == 0 || k == 0) return st;
+  if (ceil_div(n, 128) * (k / 128) > INT_MAX) return DG_ERROR_NOT_SUPPORTED;
+  CastParams p{x, ldx, static_cast<uint8_t*>(q), ldq, sf, sf_sn, sf_sk, n, k, ue8m0 ? 1 : 0};
+  return launch_per_block_cast(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
+}
+
+DG_EXPORT int dg_get_mk_alignment_for_contiguous_layout(void) { return kContiguousAlignment; }
+
+DG_EXPORT dg_status dg_set_num_cus(int num_cus) {
+  g_num_cus_override = num_cus > 0 ? num_cus : 0;
+  return DG_SUCCESS;
+}
+
+DG_EXPORT int dg_get_num_cus(void) { return device_cus(); }

@@ -1,0 +1,170 @@
+// FP8 (E4M3) quantizers: per-token 1x128 blocks (bf16 or fp32 input) and
+// per-weight 128x128 blocks (fp32 input).  Bandwidth-bound streaming kernels.
+//
+// The GEMMs take E4M3 operands with block scales; the cast is the caller's job
+// (page ssnai.com DeepGEMM analysis: no automatic FP8 casting).  Scale and code
+// rules, bit-exact:
+//   amax = max |x| over the block;  s = fl32(max(amax, 1e-4) / 448)  (IEEE division);
+//   UE8M0 mode: s rounded up to a power of two (exponent-only scales, page
+//   ssnai.com analysis, the SM100 scale-format notes);
+//   q = E4M3 RNE of clamp(fl32(x / s), +-448), sign of zero kept.
+// Block scaling and the E4M3 format: page "GitHub 推荐…DeepGEMM…", 问题判断;
+// page "企业官网建设流程全解析", section 2.3.
+//
+// Per-token layout: 16 lanes own one 128-element block (8 elements each), so a
+// wave covers 4 blocks and the block amax is a 16-lane butterfly reduction.
+#include "dgfp8_internal.h"
+
+namespace dgfp8 {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxFloor = 1e-4f;
+
+__device__ __forceinline__ float block_scale(float amax, int ue8m0) {
+  float s = fmaxf(amax, kAmaxFloor) / kE4M3Max;   // correctly rounded fp32 division
+  if (ue8m0) {
+    uint32_t u = __float_as_uint(s);
+    if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
+    s = __uint_as_float(u);
+  }
+  return s;
+}
+
+// E4M3 code of t, |t| <= 448, round to nearest even, no flush to zero.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {
+    // below 2^-6 the spacing is 2^-9: scale exactly and round to an integer 0..8
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    // keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, float s) {
+  auto one = [s](float x) {
+    float t = x / s;                              // correctly rounded fp32 division
+    t = fminf(fmaxf(t, -kE4M3Max), kE4M3Max);
+    return e4m3_rne(t);
+  };
+  return one(x0) | (one(x1) << 8) | (one(x2) << 16) | (one(x3) << 24);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <bool kF32>
+__global__ void __launch_bounds__(256) per_token_cast_kernel(CastParams p) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t kbs = p.k / 128;
+  const int64_t nblocks = p.rows * kbs;
+  for (int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16; blk < nblocks;
+       blk += (int64_t)gridDim.x * 16) {
+    const int64_t row = blk / kbs;
+    const int64_t kb = blk - row * kbs;
+    const int64_t col = kb * 128 + lane16 * 8;
+    float x[8];
+    if constexpr (kF32) {
+      const float* src = (const float*)p.x + row * p.ldx + col;
+      const f32x4 v0 = *(const f32x4*)src;
+      const f32x4 v1 = *(const f32x4*)(src + 4);
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    } else {
+      const uint16_t* src = (const uint16_t*)p.x + row * p.ldx + col;
+      const u32x4 v = *(const u32x4*)src;
+      x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+      x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const float s = block_scale(amax, p.ue8m0);
+    u32x2 out;
+    out.x = quant4(x[0], x[1], x[2], x[3], s);
+    out.y = quant4(x[4], x[5], x[6], x[7], s);
+    *(u32x2*)(p.q + row * p.ldq + col) = out;
+    if (lane16 == 0) p.sf[row * p.sf_s0 + kb * p.sf_s1] = s;
+  }
+}
+
+// One workgroup per 128x128 block: 16 lanes per row, 16 rows per pass, 8 passes.
+__global__ void __launch_bounds__(256) per_block_cast_kernel(CastParams p) {
+  const int64_t kbs = p.k / 128;
+  const int64_t nb = blockIdx.x / kbs;
+  const int64_t kb = blockIdx.x - nb * kbs;
+  const int lane16 = threadIdx.x & 15;
+  const int rsub = threadIdx.x >> 4;               // 0..15
+  const int64_t col = kb * 128 + lane16 * 8;
+  float x[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = nb * 128 + i * 16 + rsub;
+    if (row < p.rows) {
+      const float* src = (const float*)p.x + row * p.ldx + col;
+      const f32x4 v0 = *(const f32x4*)src;
+      const f32x4 v1 = *(const f32x4*)(src + 4);
+      x[i][0] = v0.x; x[i][1] = v0.y; x[i][2] = v0.z; x[i][3] = v0.w;
+      x[i][4] = v1.x; x[i][5] = v1.y; x[i][6] = v1.z; x[i][7] = v1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[i][j]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  __shared__ float wave_max[4];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float s = block_scale(amax, p.ue8m0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = nb * 128 + i * 16 + rsub;
+    if (row < p.rows) {
+      u32x2 out;
+      out.x = quant4(x[i][0], x[i][1], x[i][2], x[i][3], s);
+      out.y = quant4(x[i][4], x[i][5], x[i][6], x[i][7], s);
+      *(u32x2*)(p.q + row * p.ldq + col) = out;
+    }
+  }
+  if (threadIdx.x == 0) p.sf[nb * p.sf_s0 + kb * p.sf_s1] = s;
+}
+
+}  // namespace
+
+hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus, hipStream_t stream) {
+  const int64_t nblocks = p.rows * (p.k / 128);
+  int64_t grid = (nblocks + 15) / 16;
+  const int64_t cap = (int64_t)num_cus * 16;    // grid-stride beyond 16 workgroups per CU
+  if (grid > cap) grid = cap;
+  if (input_fp32)
+    hipLaunchKernelGGL(per_token_cast_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(per_token_cast_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_per_block_cast(const CastParams& p, hipStream_t stream) {
+  const int64_t blocks = ((p.rows + 127) / 128) * (p.k / 128);
+  hipLaunchKernelGGL(per_block_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dgfp8

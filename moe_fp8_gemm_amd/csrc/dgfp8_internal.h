@@ -1,0 +1,63 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dgfp8.h"
+
+namespace dgfp8 {
+
+enum Variant : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Everything a GEMM launch needs.  Pointers are device addresses; strides are
+// in elements (bytes for the E4M3 operands).
+struct GemmParams {
+  const uint8_t* a;
+  int64_t lda, a_gs;              // a_gs: group stride (masked)
+  const float* sfa;
+  int64_t sfa_sm, sfa_sk, sfa_gs;
+  const uint8_t* b;
+  int64_t ldb, b_gs;
+  const float* sfb;
+  int64_t sfb_sn, sfb_sk, sfb_gs;
+  uint16_t* d;
+  int64_t ldd, d_gs;
+  const int32_t* m_indices;       // contiguous
+  const int32_t* masked_m;        // masked
+  int64_t m;                      // dense: M, contiguous: m_total, masked: max_m
+  int64_t n, k;
+  int num_groups;
+};
+
+// Kernel instances the host can pick (see gemm_fp8.hip for the tile shapes).
+enum GemmInstance : int {
+  kInstLarge = 0,     // 128 x 256 output tiles, 4 waves, 3-stage LDS pipeline
+  kInstMid = 1,       // 128 x 128 output tiles, 4 waves, 4-stage LDS pipeline
+  kNumInstances
+};
+
+struct InstanceInfo {
+  int bm, bn;
+};
+InstanceInfo instance_info(GemmInstance inst);
+
+hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int grid,
+                       hipStream_t stream);
+
+struct CastParams {
+  const void* x;
+  int64_t ldx;
+  uint8_t* q;
+  int64_t ldq;
+  float* sf;
+  int64_t sf_s0, sf_s1;           // per-token: (row, kblock); per-block: (nblock, kblock)
+  int64_t rows, k;
+  int ue8m0;
+};
+
+hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus,
+                                 hipStream_t stream);
+hipError_t launch_per_block_cast(const CastParams& p, hipStream_t stream);
+
+}  // namespace dgfp8

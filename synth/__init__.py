@@ -18,14 +18,14 @@ Workloads (sizes as the workload list of the method states them):
 
 Random streams: ``numpy.random.Generator(PCG64)`` seeded from
 ``numpy.random.SeedSequence(seed)``; child 0 drives routing and A, child
-1 + g drives B of group g, so every group can be drawn on its own.  Large B
+1 + g drives B of group g, so every group can be drawn on its own.  Large
 tensors can instead be drawn on the GPU with a seeded ``torch.Generator``
-(``draw_b_device``); that stream is torch's own and differs from the host one.
+(``draw_activation_device`` / ``draw_weight_device``): same distributions,
+torch's own stream.
 """
 from __future__ import annotations
 
-import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -108,6 +108,13 @@ def layout_contiguous(counts: Sequence[int], align: int = SEGMENT_ALIGN) -> np.n
     return np.concatenate(parts) if parts else np.zeros(0, np.int32)
 
 
+def contiguous_routing(num_groups: int, tokens: int, probs: Sequence[float], seed: int):
+    """(counts [G], m_indices [m_total]) of a contiguous workload, without drawing A or B."""
+    g0, _ = _streams(seed, num_groups)
+    counts = g0.multinomial(tokens, np.asarray(probs, dtype=np.float64))
+    return counts, layout_contiguous(counts)
+
+
 def contiguous(num_groups: int, tokens: int, probs: Sequence[float], n: int, k: int,
                seed: int, draw_b: bool = True) -> Contiguous:
     g0, gb = _streams(seed, num_groups)
@@ -147,6 +154,12 @@ class Masked:
     @property
     def m_useful(self) -> int:
         return int(np.minimum(self.masked_m, self.max_m).sum())
+
+
+def masked_counts(num_groups: int, max_m: int, seed: int) -> np.ndarray:
+    """masked_m of a masked workload, without drawing A or B."""
+    g0, _ = _streams(seed, num_groups)
+    return g0.integers(0, max_m + 1, size=num_groups).astype(np.int32)
 
 
 def masked(num_groups: int, max_m: int, n: int, k: int, seed: int,
@@ -190,9 +203,22 @@ CONFIG4_NK = (4096, 7168)
 CONFIG4_CAST_SHAPE = (32768, 7168)
 
 
+def config2_routing(shape_index: int):
+    return contiguous_routing(8, 8192, [1.0 / 8] * 8, seed_for(2, shape_index))
+
+
+def config3_masked_m(shape_index: int) -> np.ndarray:
+    return masked_counts(16, 256, seed_for(3, shape_index))
+
+
+def config4_routing():
+    return contiguous_routing(CONFIG4_EXPERTS, CONFIG4_TOKENS,
+                              zipf_probs(CONFIG4_EXPERTS, CONFIG4_ZIPF_S), seed_for(4, 0))
+
+
 def config4(draw_b: bool = False) -> Contiguous:
     """Zipf-routed contiguous MoE with power-of-two scales.  B (7.5 GB of codes at
-    full size) is normally drawn per group on the device; see ``draw_b_device``."""
+    full size) is normally drawn per group on the device (``draw_weight_device``)."""
     n, k = CONFIG4_NK
     return contiguous(CONFIG4_EXPERTS, CONFIG4_TOKENS, zipf_probs(CONFIG4_EXPERTS, CONFIG4_ZIPF_S),
                       n, k, seed_for(4, 0), draw_b=draw_b)
@@ -208,10 +234,31 @@ def config4_cast_input(rows: Optional[int] = None):
     return torch.from_numpy(draw_activation(g0, r, k)).to(torch.bfloat16)
 
 
-def draw_b_device(seed: int, g: int, n: int, k: int, device):
-    """fp32 [n, k] N(0,1) drawn on ``device`` by torch's generator seeded with
-    (seed, g).  Used where host generation of B would take minutes."""
+# ---------------------------------------------------------------- device-side draws
+# For full-size problems (hundreds of millions of values) the fp32 draws are made
+# on the GPU by torch's seeded generator: same distributions as above, a
+# different (torch) stream.  Stream ids keep A, row factors and each B group apart.
+
+def _device_gen(seed: int, stream: int, device):
     import torch
     gen = torch.Generator(device=device)
-    gen.manual_seed(seed * 100003 + g)
+    gen.manual_seed((seed * 1_000_003 + stream) % (2 ** 63))
+    return gen
+
+
+def draw_activation_device(rows: int, k: int, seed: int, device, stream: int = 0):
+    """fp32 [rows, k] on ``device``: N(0,1) times fp32(2**u) per row, u ~ U[-4, 4]."""
+    import torch
+    gen = _device_gen(seed, 2 * stream, device)
+    a = torch.randn((rows, k), generator=gen, device=device, dtype=torch.float32)
+    u = torch.rand((rows,), generator=_device_gen(seed, 2 * stream + 1, device), device=device,
+                   dtype=torch.float64) * 8.0 - 4.0
+    a *= torch.exp2(u).to(torch.float32)[:, None]
+    return a
+
+
+def draw_weight_device(n: int, k: int, seed: int, group: int, device):
+    """fp32 [n, k] N(0,1) on ``device`` for group ``group``."""
+    import torch
+    gen = _device_gen(seed, 1_000_000 + group, device)
     return torch.randn((n, k), generator=gen, device=device, dtype=torch.float32)

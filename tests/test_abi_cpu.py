@@ -1,0 +1,118 @@
+"""The C-ABI library loads without a GPU, exports every function include/dgfp8.h
+declares, and its host-side validation returns the documented status codes.
+None of these calls reaches a kernel launch or any HIP runtime call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgfp8.h")
+LIB = os.path.join(ROOT, "moe_fp8_gemm_amd", "libdgfp8.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdgfp8.so not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+                     "dg_per_token_cast_fp8", "dg_get_mk_alignment_for_contiguous_layout", "dg_set_num_cus",
+                     "dg_get_num_cus", "dg_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_header():
+    import moe_fp8_gemm_amd as m
+    assert sorted(m._SIGNATURES) == _declared()
+
+
+def test_status_strings_and_constants(lib):
+    lib.dg_status_string.restype = ctypes.c_char_p
+    assert lib.dg_status_string(0) == b"DG_SUCCESS"
+    assert lib.dg_status_string(3) == b"DG_ERROR_MISALIGNED_LAYOUT"
+    assert lib.dg_get_mk_alignment_for_contiguous_layout() == 128
+
+
+# Fake, never-dereferenced, 256-aligned addresses: validation must reject the
+# call before anything touches them.
+P = ctypes.c_void_p(0x10000)
+
+
+def _gemm(lib, a=P, lda=512, sfa=P, sfa_sm=4, sfa_sk=1, b=P, ldb=512, sfb=P, sfb_sn=4, sfb_sk=1,
+          d=P, ldd=256, m=128, n=256, k=512):
+    f = lib.dg_fp8_gemm_nt
+    i = ctypes.c_int64
+    return f(a, i(lda), sfa, i(sfa_sm), i(sfa_sk), b, i(ldb), sfb, i(sfb_sn), i(sfb_sk), d, i(ldd),
+             i(m), i(n), i(k), None)
+
+
+def test_dense_validation(lib):
+    assert _gemm(lib, a=None) == 1                       # null -> INVALID_VALUE
+    assert _gemm(lib, m=-1) == 1
+    assert _gemm(lib, lda=256) == 1                      # lda < k
+    assert _gemm(lib, sfa_sk=-1) == 1
+    assert _gemm(lib, k=384 + 64, lda=512, ldb=512) == 2  # k % 128 -> NOT_SUPPORTED
+    assert _gemm(lib, n=252, ldd=256) == 2               # n % 8
+    assert _gemm(lib, lda=520) == 2                      # lda % 16
+    assert _gemm(lib, a=ctypes.c_void_p(0x10008)) == 2   # misaligned A
+    assert _gemm(lib, m=0) == 0                          # empty problem: success, no launch
+    assert _gemm(lib, n=0) == 0
+
+
+def test_contiguous_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    i = ctypes.c_int64
+
+    def call(m_total=256, groups=2, m_idx=P, n=256, k=512):
+        return f(P, i(512), P, i(4), i(1), P, i(512), i(256 * 512), P, i(4), i(1), i(8), P, i(256),
+                 m_idx, i(m_total), i(n), i(k), ctypes.c_int(groups), None)
+
+    assert call(m_total=200) == 3                        # MISALIGNED_LAYOUT
+    assert call(groups=0) == 1
+    assert call(m_idx=None) == 1
+    assert call(k=500) == 2
+    assert call(m_total=0) == 0
+
+
+def test_masked_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked
+    i = ctypes.c_int64
+
+    def call(groups=4, max_m=256, mm=P, k=512):
+        return f(P, i(512), i(256 * 512), P, i(4), i(1), i(1024), P, i(512), i(256 * 512), P, i(4), i(1),
+                 i(8), P, i(256), i(256 * 256), mm, ctypes.c_int(groups), i(max_m), i(256), i(k), i(128), None)
+
+    assert call(groups=0) == 1
+    assert call(groups=2000) == 2                        # beyond the device-side group limit
+    assert call(mm=None) == 1
+    assert call(k=100) == 2
+    assert call(max_m=0) == 0
+
+
+def test_cast_validation(lib):
+    i = ctypes.c_int64
+    f = lib.dg_per_token_cast_fp8
+    assert f(P, i(512), P, i(512), P, i(4), i(1), i(8), i(500), 0, None) == 2   # k % 128
+    assert f(P, i(256), P, i(512), P, i(4), i(1), i(8), i(512), 0, None) == 1   # ldx < k
+    assert f(P, i(520), P, i(520), P, i(4), i(1), i(8), i(512), 0, None) == 2   # ldx*2 % 16 ok, ldq % 16 not
+    assert f(None, i(512), P, i(512), P, i(4), i(1), i(8), i(512), 0, None) == 1
+    assert f(P, i(512), P, i(512), P, i(4), i(1), i(0), i(512), 0, None) == 0
+    g = lib.dg_per_block_cast_fp8
+    assert g(P, i(512), P, i(512), P, i(4), i(1), i(8), i(100), 0, None) == 2

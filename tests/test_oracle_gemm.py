@@ -155,6 +155,15 @@ def test_sampled_matches_full():
     assert np.array_equal(gemm.gemm_nt_sampled(a, sfa, b, sfb, rows, cols), full[np.ix_(rows, cols)])
 
 
+def test_columns_form_matches_full():
+    rng = np.random.default_rng(29)
+    a, sfa, b, sfb = _problem(rng, 9, 260, 384)
+    full = gemm.gemm_nt(a, sfa, b, sfb)
+    cols = np.array([0, 127, 128, 259])
+    got = gemm.gemm_nt_columns(a[[2, 8]], sfa[[2, 8]], b[cols], sfb[cols // 128])
+    assert np.array_equal(got, full[np.ix_([2, 8], cols)])
+
+
 def test_contiguous_rows_follow_their_group_and_padding_is_untouched():
     rng = np.random.default_rng(27)
     g, n, k = 3, 64, 256

@@ -61,6 +61,19 @@ def gemm_nt_sampled(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarr
     return round_to_bf16_bits(a64 @ b64.T)
 
 
+def gemm_nt_columns(a_rows: np.ndarray, sfa_rows: np.ndarray, b_rows: np.ndarray,
+                    sfb_rows: np.ndarray) -> np.ndarray:
+    """D for some rows of A and some output columns, given directly.
+
+    a_rows [R, K] with sfa_rows [R, K/128]; b_rows [C, K] are the B rows of the
+    wanted output columns and sfb_rows [C, K/128] the scales of the 128-row
+    block each of them belongs to.  Returns bf16 bits [R, C].
+    """
+    a64 = dequantize_rows(a_rows, sfa_rows)
+    b64 = dequantize_rows(b_rows, sfb_rows)
+    return round_to_bf16_bits(a64 @ b64.T)
+
+
 def m_grouped_contiguous(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarray,
                          m_indices: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
     """Row i with g = m_indices[i] >= 0 gets the dense result against B[g];

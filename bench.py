@@ -1,0 +1,285 @@
+"""Benchmark of the FP8 block-scaled GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+A step is one pass over the dense LLM-layer workload: the 15 GEMMs
+M in {64, 128, 4096} x (N, K) in {(2112,7168), (24576,1536), (7168,16384),
+(4096,7168), (7168,2048)}, inputs quantized once (device-side fp32 draws, the
+library's own cast kernels) and resident in HBM before timing.  ``value`` is
+whole-step TFLOPS (2*M*N*K summed over the step / wall time of K steps).
+
+The JSON line also carries:
+* ``roofline``: the dominant kernel (the 128x256-tile dense instance, which runs
+  the M=4096 shapes), algorithmic FLOPs per launch / its average launch time
+  measured with HIP events on the launch stream inside the timed steps, against
+  the 5.0 PFLOP/s dense FP8 MFMA peak;
+* ``cpu_baseline``: the CPU oracle timed on the full 4096x4096x7168 GEMM (4 runs);
+* ``extras``: cold-cache per-shape times, the MoE workloads (contiguous G=8,
+  masked G=16, Zipf contiguous G=256 with power-of-two scales) and the per-token
+  cast of a bf16 [32768, 7168] activation in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_dense(dg, m, n, k, seed, dev):
+    a32 = synth.draw_activation_device(m, k, seed, dev)
+    b32 = synth.draw_weight_device(n, k, seed, 0, dev)
+    qa, sa = dg.per_token_cast_fp8(a32)
+    qb, sb = dg.per_block_cast_fp8(b32)
+    del a32, b32
+    d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    return (qa, sa), (qb, sb), d
+
+
+class Flusher:
+    """Overwrites a buffer larger than the MALL so that cold-cache timings do not
+    see operands left in the 256 MB Infinity Cache."""
+
+    def __init__(self, dev, nbytes=1 << 30):
+        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def event_time_ms(fn, reps, flush=None):
+    times = []
+    for _ in range(reps):
+        if flush:
+            flush()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    return float(np.median(times))
+
+
+def bench_extras(dg, dev, reps):
+    out = {}
+    flush = Flusher(dev)
+    # --- contiguous G=8 (prefill) and masked G=16 (decode)
+    for idx, (n, k) in enumerate(synth.GROUPED_NK):
+        counts, m_indices = synth.config2_routing(idx)
+        seed = synth.seed_for(2, idx)
+        m_total = m_indices.size
+        valid = torch.as_tensor(np.nonzero(m_indices >= 0)[0], device=dev)
+        a32 = torch.zeros((m_total, k), dtype=torch.float32, device=dev)
+        a32[valid] = synth.draw_activation_device(int(valid.numel()), k, seed, dev)
+        qa, sa = dg.per_token_cast_fp8(a32)
+        del a32
+        qb = torch.empty((8, n, k), dtype=torch.float8_e4m3fn, device=dev)
+        sb = torch.empty((8, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
+        for g in range(8):
+            dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), q=qb[g], sf=sb[g])
+        d = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
+        mi = torch.from_numpy(m_indices).to(dev)
+        ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi), reps, flush)
+        useful = 2.0 * int(counts.sum()) * n * k
+        out[f"contiguous_G8_{n}x{k}"] = {
+            "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
+            "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "m_total": m_total}
+        del qa, sa, qb, sb, d
+
+        masked_m = synth.config3_masked_m(idx)
+        seed = synth.seed_for(3, idx)
+        a32 = synth.draw_activation_device(16 * 256, k, seed, dev)
+        qa, sa = dg.per_token_cast_fp8(a32)
+        del a32
+        qb = torch.empty((16, n, k), dtype=torch.float8_e4m3fn, device=dev)
+        sb = torch.empty((16, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
+        for g in range(16):
+            dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), q=qb[g], sf=sb[g])
+        d = torch.empty((16, 256, n), dtype=torch.bfloat16, device=dev)
+        mm = torch.from_numpy(masked_m).to(dev)
+        qa3, sa3 = qa.view(16, 256, k), sa.view(16, 256, k // 128)
+        ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa3, sa3), (qb, sb), d, mm, 128), reps, flush)
+        useful = 2.0 * int(masked_m.sum()) * n * k
+        b_bytes = 16 * n * k
+        out[f"masked_G16_{n}x{k}"] = {
+            "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS,
+            "b_read_gbs": b_bytes / ms / 1e6}
+        del qa, sa, qb, sb, d
+    # --- Zipf contiguous G=256, power-of-two scales
+    counts, m_indices = synth.config4_routing()
+    n, k = synth.CONFIG4_NK
+    seed = synth.seed_for(4, 0)
+    m_total = m_indices.size
+    valid = torch.as_tensor(np.nonzero(m_indices >= 0)[0], device=dev)
+    a32 = torch.zeros((m_total, k), dtype=torch.float32, device=dev)
+    a32[valid] = synth.draw_activation_device(int(valid.numel()), k, seed, dev)
+    qa, sa = dg.per_token_cast_fp8(a32, ue8m0=True)
+    del a32
+    qb = torch.empty((256, n, k), dtype=torch.float8_e4m3fn, device=dev)
+    sb = torch.empty((256, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
+    for g in range(256):
+        dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), ue8m0=True, q=qb[g], sf=sb[g])
+    d = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
+    mi = torch.from_numpy(m_indices).to(dev)
+    ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi), max(3, reps // 2), flush)
+    useful = 2.0 * int(counts.sum()) * n * k
+    out["contiguous_zipf_G256_4096x7168_ue8m0"] = {
+        "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
+        "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "b_read_gbs": 256 * n * k / ms / 1e6,
+        "m_total": m_total}
+    del qa, sa, qb, sb, d
+    # --- per-token cast of the bf16 activation
+    x = synth.config4_cast_input().to(dev)
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
+    s = torch.empty((x.shape[0], x.shape[1] // 128), dtype=torch.float32, device=dev)
+    elems = x.numel()
+    for ue in (False, True):
+        ms = event_time_ms(lambda: dg.per_token_cast_fp8(x, ue8m0=ue, q=q, sf=s), reps, flush)
+        nbytes = elems * (2 + 1) + elems // 128 * 4
+        out[f"per_token_cast_bf16_32768x7168{'_ue8m0' if ue else ''}"] = {
+            "us": ms * 1e3, "gbs": nbytes / ms / 1e6, "pct_hbm_peak": 100 * nbytes / ms / 1e6 / HBM_PEAK_GBS}
+    return out
+
+
+def cpu_baseline():
+    """The oracle as it stands, on the full 4096x4096x7168 GEMM of the workload (4 runs)."""
+    from threadpoolctl import threadpool_info
+    from oracle import gemm as ogemm
+    from oracle import quant
+    m, n, k = 4096, 4096, 7168
+    idx = synth.config1_shapes().index((m, n, k))
+    w = synth.config1(idx)
+    qa, sa = quant.per_token_cast(w.a)
+    qb, sb = quant.per_block_cast(w.b)
+    del w
+    reps = 4
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ogemm.gemm_nt(qa, sa, qb, sb)
+    dt = (time.perf_counter() - t0) / reps
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    return {"value": 2.0 * m * n * k / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full {m}x{n}x{k} GEMM of the workload, {reps} times (decode, float64 BLAS matmul, "
+                      f"bf16 rounding): {dt:.2f} s each; BLAS threads {threads}, host cores "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU (expert-parallel) runs are not part of "
+              "this build -- use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import moe_fp8_gemm_amd as dg
+
+    dev = torch.device("cuda:0")
+    shapes = synth.config1_shapes()
+    log("preparing inputs")
+    probs = []
+    for i, (m, n, k) in enumerate(shapes):
+        probs.append(make_dense(dg, m, n, k, synth.seed_for(1, i), dev))
+    torch.cuda.synchronize()
+    flops = [2.0 * m * n * k for (m, n, k) in shapes]
+    big = [i for i, (m, _, _) in enumerate(shapes) if m == 4096]
+
+    def step(events=None):
+        for i, (a, b, d) in enumerate(probs):
+            if events is not None:
+                events[i][0].record()
+            dg.fp8_gemm_nt(a, b, d)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in shapes] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+    per_launch = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(shapes))]
+                           for s in range(args.steps)])      # ms
+    mean_ms = per_launch.mean(axis=0)
+    dom_time = float(mean_ms[big].mean())                    # average launch duration of the big-tile kernel
+    dom_flops = float(np.mean([flops[i] for i in big]))      # algorithmic FLOPs per launch (mean over its launches)
+    achieved = dom_flops / (dom_time * 1e-3) / 1e12
+    per_shape = []
+    for i, (m, n, k) in enumerate(shapes):
+        per_shape.append({"m": m, "n": n, "k": k, "us_in_step": float(mean_ms[i] * 1e3),
+                          "tflops": flops[i] / (mean_ms[i] * 1e-3) / 1e12})
+    log("cold-cache per-shape times")
+    flush = Flusher(dev)
+    for i, (a, b, d) in enumerate(probs):
+        ms = event_time_ms(lambda: dg.fp8_gemm_nt(a, b, d), 10, flush)
+        per_shape[i]["us_cold"] = ms * 1e3
+        per_shape[i]["tflops_cold"] = flops[i] / (ms * 1e-3) / 1e12
+        per_shape[i]["pct_fp8_peak_cold"] = 100 * per_shape[i]["tflops_cold"] / FP8_PEAK_TFLOPS
+    del flush
+    result = {
+        "metric": "FP8 block-scaled GEMM TFLOPS (1 GPU) and % of MI355X FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic (seeded device-side N(0,1) draws, log-uniform row factors; quantized by the library casts)",
+        "config": {"workload": "dense fp8_gemm_nt, LLM-layer shapes: M in {64,128,4096} x (N,K) in "
+                               "{(2112,7168),(24576,1536),(7168,16384),(4096,7168),(7168,2048)}; "
+                               "A 1x128 and B 128x128 fp32 block scales, bf16 out",
+                   "gemms_per_step": len(shapes), "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel<Cfg<128,256,2,2,3>, dense> on the five M=4096 shapes",
+                     "avg_launch_us": round(dom_time * 1e3, 2), "flops_per_launch": dom_flops},
+        "per_shape": per_shape,
+    }
+    if not args.no_extras:
+        log("extras: MoE workloads and cast")
+        del probs
+        torch.cuda.empty_cache()
+        result["extras"] = bench_extras(dg, dev, reps=10)
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profiling aid: time only this M,N,K of the workload (e.g. 4096,4096,7168)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; multi-GPU (expert-parallel) runs are not part of "
@@ -199,13 +201,19 @@ def main():
 
     dev = torch.device("cuda:0")
     shapes = synth.config1_shapes()
+    if args.only:
+        want = tuple(int(x) for x in args.only.split(","))
+        if want not in shapes:
+            sys.exit(f"--only {args.only} is not one of the workload's shapes")
+        shapes = [want]
     log("preparing inputs")
     probs = []
-    for i, (m, n, k) in enumerate(shapes):
-        probs.append(make_dense(dg, m, n, k, synth.seed_for(1, i), dev))
+    for (m, n, k) in shapes:
+        idx = synth.config1_shapes().index((m, n, k))
+        probs.append(make_dense(dg, m, n, k, synth.seed_for(1, idx), dev))
     torch.cuda.synchronize()
     flops = [2.0 * m * n * k for (m, n, k) in shapes]
-    big = [i for i, (m, _, _) in enumerate(shapes) if m == 4096]
+    big = [i for i, (m, _, _) in enumerate(shapes) if m == 4096] or list(range(len(shapes)))
 
     def step(events=None):
         for i, (a, b, d) in enumerate(probs):

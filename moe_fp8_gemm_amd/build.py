@@ -34,9 +34,16 @@ def _flags():
             "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  The GEMM promotes every MFMA result with VALU FMAs, so
+# MFMA results must land in VGPRs: force the VGPR-destination MFMA form (LLVM
+# otherwise picks the AGPR form for kernels allowed more than 256 VGPRs, and each
+# result then needs extra v_accvgpr_read moves).
+EXTRA_FLAGS = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -51,11 +51,34 @@ dg_status check_common(const void* a, int64_t lda, const float* sfa, int64_t sfa
   return DG_SUCCESS;
 }
 
-// Static instance table: the wide 128x256 tile when it already yields at least
-// one tile per CU, else the 128x128 tile for more parallelism.
-GemmInstance choose_instance(int64_t m_tiles_128, int64_t n, int cus) {
-  const int64_t wide_tiles = m_tiles_128 * ((n + 255) / 256);
-  return wide_tiles >= cus ? kInstLarge : kInstMid;
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Static instance choice: estimated time = rounds of persistent tiles x tile
+// area x a per-instance cost factor (relative cycles per output element,
+// measured on MI355X: bigger tiles move fewer bytes through L2 and LDS per FLOP).
+double instance_cost(GemmInstance inst, int64_t m_rows, int64_t groups_m_tiles_hint, int64_t n, int cus) {
+  const InstanceInfo info = instance_info(inst);
+  const int64_t tiles = (groups_m_tiles_hint > 0 ? groups_m_tiles_hint : ceil_div(m_rows, info.bm)) *
+                        ceil_div(n, info.bn);
+  const int64_t rounds = ceil_div(tiles, cus);
+  const double factor = inst == kInstHuge ? 1.0 : (inst == kInstLarge ? 1.2 : 1.5);
+  return (double)rounds * info.bm * info.bn * factor;
+}
+
+GemmInstance choose_dense(int64_t m, int64_t n, int cus) {
+  GemmInstance best = kInstMid;
+  double best_cost = instance_cost(kInstMid, m, 0, n, cus);
+  for (GemmInstance inst : {kInstLarge, kInstHuge}) {
+    const double c = instance_cost(inst, m, 0, n, cus);
+    if (c < best_cost) { best = inst; best_cost = c; }
+  }
+  return best;
+}
+
+// Contiguous layout: the group of a tile is read per 128 rows, so BM = 128.
+GemmInstance choose_contiguous(int64_t m_total, int64_t n, int cus) {
+  return instance_cost(kInstLarge, m_total, 0, n, cus) <= instance_cost(kInstMid, m_total, 0, n, cus)
+             ? kInstLarge : kInstMid;
 }
 
 dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile_bound, hipStream_t stream) {
@@ -66,7 +89,11 @@ dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile
   return launch_gemm(inst, v, p, (int)grid, stream) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// The kernels address one group's operand rows with 32-bit byte offsets.
+bool offsets_fit(int64_t rows_a, int64_t lda, int64_t n, int64_t ldb) {
+  const int64_t lim = (int64_t)UINT32_MAX;
+  return (rows_a - 1) * lda + lda <= lim && (n - 1) * ldb + ldb <= lim;
+}
 
 }  // namespace
 }  // namespace dgfp8
@@ -91,6 +118,7 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
   if (m == 0 || n == 0) return DG_SUCCESS;
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
   if (st != DG_SUCCESS) return st;
+  if (!offsets_fit(m, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
   p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
@@ -98,7 +126,7 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
   p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
-  const GemmInstance inst = choose_instance(ceil_div(m, 128), n, device_cus());
+  const GemmInstance inst = choose_dense(m, n, device_cus());
   const InstanceInfo info = instance_info(inst);
   const int64_t tiles = ceil_div(m, info.bm) * ceil_div(n, info.bn);
   return launch(inst, kDense, p, tiles, static_cast<hipStream_t>(stream));
@@ -118,6 +146,7 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
   if (st != DG_SUCCESS) return st;
   if (b_group_stride % 16 != 0 || !aligned(m_indices, 4)) return DG_ERROR_NOT_SUPPORTED;
+  if (!offsets_fit(m_total, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
   p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
@@ -126,7 +155,7 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m_indices = m_indices;
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
-  const GemmInstance inst = choose_instance(m_total / 128, n, device_cus());
+  const GemmInstance inst = choose_contiguous(m_total, n, device_cus());
   const InstanceInfo info = instance_info(inst);
   const int64_t tiles = (m_total / info.bm) * ceil_div(n, info.bn);
   return launch(inst, kContiguous, p, tiles, static_cast<hipStream_t>(stream));
@@ -152,6 +181,7 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
   if (st != DG_SUCCESS) return st;
   if (a_group_stride % 16 != 0 || b_group_stride % 16 != 0 || d_group_stride % 8 != 0 || !aligned(masked_m, 4))
     return DG_ERROR_NOT_SUPPORTED;
+  if (!offsets_fit(max_m, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda; p.a_gs = a_group_stride;
   p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk; p.sfa_gs = sfa_group_stride;
@@ -160,7 +190,9 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd; p.d_gs = d_group_stride;
   p.masked_m = masked_m;
   p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
-  const GemmInstance inst = choose_instance((int64_t)num_groups * ceil_div(max_m, 128), n, device_cus());
+  // Masked decode streams each group's B once per M tile: a 256-row tile covers
+  // groups of up to 256 rows in one pass.
+  const GemmInstance inst = max_m > 128 ? kInstHuge : kInstLarge;
   const InstanceInfo info = instance_info(inst);
   const int64_t bound = (int64_t)num_groups * ceil_div(max_m, info.bm) * ceil_div(n, info.bn);
   return launch(inst, kMasked, p, bound, static_cast<hipStream_t>(stream));

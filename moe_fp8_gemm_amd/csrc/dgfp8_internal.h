@@ -32,8 +32,9 @@ struct GemmParams {
 
 // Kernel instances the host can pick (see gemm_fp8.hip for the tile shapes).
 enum GemmInstance : int {
-  kInstLarge = 0,     // 128 x 256 output tiles, 4 waves, 3-stage LDS pipeline
-  kInstMid = 1,       // 128 x 128 output tiles, 4 waves, 4-stage LDS pipeline
+  kInstLarge = 0,     // 128 x 256 output tiles, 8 waves, 3-stage LDS pipeline
+  kInstMid = 1,       // 128 x 128 output tiles, 8 waves, 3-stage LDS pipeline
+  kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
   kNumInstances
 };
 

@@ -20,11 +20,11 @@
 //    lane needs one sa value per 16-row sub-tile, and its 4*NS columns are
 //    made contiguous by the order in which B rows are placed in LDS
 //    ("fragment order"), which turns the epilogue into 16-byte stores.
-//  * Global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4), one
-//    __shared__ buffer per pipeline stage so that the compiler's LDS-DMA
-//    wait tracking distinguishes stages; STAGES-1 K blocks are in flight while
-//    one is consumed.  Rows are XOR-swizzled in 16-byte slots to keep the
-//    fragment reads free of bank conflicts.
+//  * Global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4) into three
+//    LDS stages: while K block kb is multiplied, the DMAs of kb+1 and kb+2 are
+//    in flight.  The DMAs are waited for explicitly (s_waitcnt vmcnt) and the
+//    stage hand-over uses an LDS-only barrier.  Rows are XOR-swizzled in
+//    16-byte slots to keep the fragment reads free of bank conflicts.
 //  * Persistent grid of one workgroup per CU; the tile index sequence is remapped
 //    so that the 32 workgroups of one XCD work on neighbouring tiles (L2 per XCD).
 #include "dgfp8_internal.h"
@@ -44,34 +44,58 @@ constexpr int kKBlock = 128;      // width of a scale block along K == K of one 
 constexpr int kMaxMaskedGroups = 1024;
 constexpr int kGroupM = 8;        // raster: tiles of kGroupM consecutive M-tiles sweep N together
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt == 0, expcnt unconstrained.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= VM, lgkmcnt == 0, expcnt unconstrained.
 template <int VM>
 struct WaitVmLgkm0 {
   static constexpr int value = (VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8);
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte slot permutation of an LDS row.  Depends on the row's low 4 bits only,
+// so every 16-row fragment sees the same per-lane pattern (reads use immediate
+// offsets) and its 16 reads of one logical slot hit 16 distinct (bank-half, slot)
+// pairs: conflict-free whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int swz16(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ void dma16(const void* g, DG_LAS void* l) {
-  __builtin_amdgcn_global_load_lds((DG_GAS void*)g, l, 16, 0, 0);
+// Direct-to-LDS loads.  Issued as inline asm so that the compiler's wait-count
+// pass does not track them (it merges DMA histories conservatively at loop
+// headers and would wait for every DMA before each LDS read); the kernel waits
+// for them explicitly with s_waitcnt vmcnt.  No register is written by these
+// instructions: the data goes to LDS at M0 + 16 * lane (resp. 4 * lane).
+__device__ __forceinline__ uint32_t lds_addr(const DG_LAS void* p) {
+  return (uint32_t)(uintptr_t)p;
 }
-__device__ __forceinline__ void dma4(const void* g, DG_LAS void* l) {
-  __builtin_amdgcn_global_load_lds((DG_GAS void*)g, l, 4, 0, 0);
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const float* vaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds), "v"(vaddr) : "memory", "m0");
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; overflow gives inf).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Workgroup barrier that orders LDS accesses only (lgkmcnt), leaving DMA and
+// other vector-memory counters alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int LAG_ = 2, int BBUF_ = 3>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int kStages = STAGES_;   // LDS stages; K blocks in flight = kStages - 1
+  static constexpr int kLag = LAG_;         // MFMAs between an MFMA and the FMAs promoting it
+  static constexpr int kBBuf = BBUF_;       // B fragments held in registers (streamed)
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -83,140 +107,165 @@ struct Cfg {
   static constexpr int kNSB = BN >= 128 ? BN / 128 : 1;  // B scales per tile and K block
   static constexpr int kSAPerWave = BM / kWaves;
   static constexpr int kLoadsPerStage = kAChunksPerWave + kBChunksPerWave + 1;
-  static constexpr int kScaleFloats = BM + 4;
+  // Scale slots: wave w's DMA fills ls[64w + lane]; lane < kSAPerWave holds the A
+  // scale of tile row w*kSAPerWave + lane, the last wave's lanes kSAPerWave + j
+  // hold the B scale of 128-column block j.  Other lanes land in unused slots.
+  static constexpr int kScaleFloats = 64 * kWaves;
+  static constexpr int kMfmas = MS * NS;
   static_assert(kAChunks % kWaves == 0 && kBChunks % kWaves == 0, "chunks per wave");
   static_assert(kSAPerWave + kNSB <= 64, "scale DMA of the last wave");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one 128-column scale block");
   static_assert(NS % 2 == 0, "epilogue stores 8 columns at a time");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(kStages == 2 || kStages == 3, "pipeline depth");
 };
 
-// One LDS buffer per (config, stage, kind): distinct variables, so the compiler's
-// LDS-DMA dependency tracking keeps the stages apart.
-template <class C, int S>
+// LDS buffers, one variable per (config, variant, stage, kind): every kernel owns
+// its buffers, and distinct variables let the compiler's LDS-DMA wait tracking
+// tell the stages apart (otherwise each LDS read would wait for every DMA).
+template <class C, int V, int S>
 __device__ __forceinline__ DG_LAS uint8_t* lds_a() {
   __shared__ __attribute__((aligned(1024))) uint8_t buf[C::BM * kKBlock];
   return (DG_LAS uint8_t*)buf;
 }
-template <class C, int S>
+template <class C, int V, int S>
 __device__ __forceinline__ DG_LAS uint8_t* lds_b() {
   __shared__ __attribute__((aligned(1024))) uint8_t buf[C::BN * kKBlock];
   return (DG_LAS uint8_t*)buf;
 }
-template <class C, int S>
+template <class C, int V, int S>
 __device__ __forceinline__ DG_LAS float* lds_s() {
   __shared__ __attribute__((aligned(16))) float buf[C::kScaleFloats];
   return (DG_LAS float*)buf;
 }
 
-// Per-tile state of one workgroup (all values wave-uniform except the pointers).
+// DMA sources of one tile.  Bases are wave-uniform (scalar registers); per-lane
+// parts are 32-bit byte offsets, so the loads use the saddr + voffset form.
 template <class C>
-struct Tile {
-  const uint8_t* a_src[C::kAChunksPerWave];   // this lane's A source at K block 0
-  const uint8_t* b_src[C::kBChunksPerWave];   // this lane's B source at K block 0
-  const float* sa_src;                        // this lane's scale source at K block 0 (or null)
-  int64_t s_kstride;                          // K-block stride of that scale source
+struct TileSrc {
+  const uint8_t* a_base;
+  const uint8_t* b_base;
+  uint32_t a_off[C::kAChunksPerWave];
+  uint32_t b_off[C::kBChunksPerWave];
+  const float* s_src;       // this lane's scale at K block 0 (A row scale or B block scale)
+  int64_t s_kstride;
 };
 
-template <class C, int S>
-__device__ __forceinline__ void issue_stage(const Tile<C>& t, int kb) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  DG_LAS uint8_t* la = lds_a<C, S>();
-  DG_LAS uint8_t* lb = lds_b<C, S>();
-  DG_LAS float* ls = lds_s<C, S>();
-  const int64_t koff = (int64_t)kb * kKBlock;
-#pragma unroll
-  for (int j = 0; j < C::kAChunksPerWave; ++j)
-    dma16(t.a_src[j] + koff, la + (wave * C::kAChunksPerWave + j) * 1024);
-#pragma unroll
-  for (int j = 0; j < C::kBChunksPerWave; ++j)
-    dma16(t.b_src[j] + koff, lb + (wave * C::kBChunksPerWave + j) * 1024);
-  // Scales: wave w fetches sa of rows [w*kSAPerWave, +kSAPerWave); the last wave's
-  // next kNSB lanes fetch the B scales, which land at ls[BM + j].
-  const int active = C::kSAPerWave + (wave == C::kWaves - 1 ? C::kNSB : 0);
-  if (lane < active) dma4(t.sa_src + kb * t.s_kstride, ls + wave * C::kSAPerWave);
+// DMA instruction d (0 <= d < kLoadsPerStage) of this wave's share of K block kb
+// into LDS stage S: A chunks first, then B chunks, then the scales.
+template <class C, int V, int S>
+__device__ __forceinline__ void issue_dma_part(const TileSrc<C>& t, int kb, int wave, int lane, int d) {
+  constexpr int NA = C::kAChunksPerWave, NB = C::kBChunksPerWave;
+  (void)lane;
+  if (d < NA) {
+    dma16(t.a_base + (int64_t)kb * kKBlock, t.a_off[d], lds_addr(lds_a<C, V, S>()) + (wave * NA + d) * 1024);
+  } else if (d < NA + NB) {
+    const int j = d - NA;
+    dma16(t.b_base + (int64_t)kb * kKBlock, t.b_off[j], lds_addr(lds_b<C, V, S>()) + (wave * NB + j) * 1024);
+  } else {
+    dma4(t.s_src + kb * t.s_kstride, lds_addr(lds_s<C, V, S>()) + wave * 64 * 4);
+  }
 }
 
-// Consume one stage: MS x NS MFMAs, each promoted at once into acc.
-template <class C, int S>
-__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], int wr, int wc) {
-  const int lane = threadIdx.x & 63;
-  const int r16 = lane & 15;
-  const int q = lane >> 4;
-  DG_LAS uint8_t* la = lds_a<C, S>();
-  DG_LAS uint8_t* lb = lds_b<C, S>();
-  DG_LAS float* ls = lds_s<C, S>();
-
-  const float sb = ls[C::BM + (wc * C::WN) / 128];
-  i32x8 bf[C::NS];
+template <class C, int V, int S>
+__device__ __forceinline__ void issue_dma(const TileSrc<C>& t, int kb, int wave, int lane) {
 #pragma unroll
-  for (int t = 0; t < C::NS; ++t) {
-    const int row = wc * C::WN + t * 16 + r16;
-    DG_LAS uint8_t* base = lb + row * kKBlock;
-    const i32x4 lo = *(DG_LAS i32x4*)(base + (((2 * q) ^ swz(row)) << 4));
-    const i32x4 hi = *(DG_LAS i32x4*)(base + (((2 * q + 1) ^ swz(row)) << 4));
-    bf[t] = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  }
+  for (int d = 0; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, S>(t, kb, wave, lane, d);
+}
+
+__device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, uint32_t off1) {
+  const i32x4 lo = *(DG_LAS i32x4*)(base + off0);
+  const i32x4 hi = *(DG_LAS i32x4*)(base + off1);
+  return (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// One K block from LDS stage S.  MFMA order: B fragment t outer, A fragment ms
+// inner; A fragments and row scales are read once, B fragments stream through
+// three register buffers (fragment t+2 is read while t is multiplied).  The
+// promotion of MFMA j (4 FMAs) is issued after MFMA j+2: by then the result is
+// ready, the FMAs fill the wait states the MFMA would otherwise need, and the
+// matrix core always has the next MFMA queued.  sched_barrier(0) between the
+// groups keeps the compiler's scheduler from undoing that order.
+// off0/off1: this lane's byte offsets of its two 16-byte slots inside a 16-row
+// fragment (the same for A and B fragments).
+// The DMA of a later K block (kbd into stage SD) is spread over the MFMA
+// sequence, one instruction every kDmaGap MFMAs: issued back to back after the
+// barrier, the address unit would take them one by one and hold the waves at
+// issue, leaving the matrix cores idle.  No branches here: past the last K block
+// the caller passes the last block again (a harmless reload into a free stage).
+template <class C, int V, int S, int SD>
+__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], uint32_t off0, uint32_t off1, int wr,
+                                              int wc, int r16, const TileSrc<C>& tsrc, int kbd, int wave,
+                                              int lane) {
+  constexpr int kDmaGap = C::kMfmas / C::kLoadsPerStage > 0 ? C::kMfmas / C::kLoadsPerStage : 1;
+  constexpr int kLag = C::kLag;
+  constexpr int kBBuf = C::kBBuf;
+  DG_LAS uint8_t* la = lds_a<C, V, S>() + wr * C::WM * kKBlock;
+  DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
+  DG_LAS float* ls = lds_s<C, V, S>();
+  i32x8 af[C::MS];
+  float s[C::MS];
+  i32x8 bf[kBBuf];
+  const float sb = ls[(C::kWaves - 1) * 64 + C::kSAPerWave + (wc * C::WN) / 128];
+#pragma unroll
+  for (int ms = 0; ms < C::MS; ++ms) af[ms] = read_frag(la + ms * 16 * kKBlock, off0, off1);
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
     const int row = wr * C::WM + ms * 16 + r16;
-    DG_LAS uint8_t* base = la + row * kKBlock;
-    const i32x4 lo = *(DG_LAS i32x4*)(base + (((2 * q) ^ swz(row)) << 4));
-    const i32x4 hi = *(DG_LAS i32x4*)(base + (((2 * q + 1) ^ swz(row)) << 4));
-    const i32x8 af = (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const float s = ls[row] * sb;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    s[ms] = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
+  }
 #pragma unroll
-    for (int t = 0; t < C::NS; ++t) {
+  for (int t = 0; t < kBBuf - 1 && t < C::NS; ++t) bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
+#pragma unroll
+  for (int ms = 0; ms < C::MS; ++ms) s[ms] *= sb;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 p[kLag + 1];
+  constexpr int kM = C::kMfmas;
+#pragma unroll
+  for (int j = 0; j < kM + kLag; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < kM) {
+      const int t = j / C::MS, ms = j % C::MS;
       // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
-      // D[m = row of lane l%16][n = 4*(l/16)+r-th row of fragment t].
-      const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[t], af, zero, 0, 0, 0, 0, 0, 0);
-      acc[ms][t][0] = __builtin_fmaf(p[0], s, acc[ms][t][0]);
-      acc[ms][t][1] = __builtin_fmaf(p[1], s, acc[ms][t][1]);
-      acc[ms][t][2] = __builtin_fmaf(p[2], s, acc[ms][t][2]);
-      acc[ms][t][3] = __builtin_fmaf(p[3], s, acc[ms][t][3]);
+      // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
+      p[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[t % kBBuf], af[ms], zero,
+                                                                          0, 0, 0, 0, 0, 0);
+      const int tn = t + kBBuf - 1;
+      if (ms == 0 && tn < C::NS) bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
+      if (j % kDmaGap == 0 && j / kDmaGap < C::kLoadsPerStage)
+        issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, j / kDmaGap);
+    }
+    if (j >= kLag) {
+      const int i = j - kLag;
+      const int t = i / C::MS, ms = i % C::MS;
+      f32x4& a = acc[ms][t];
+      const f32x4 q = p[i % (kLag + 1)];
+      a[0] = __builtin_fmaf(q[0], s[ms], a[0]);
+      a[1] = __builtin_fmaf(q[1], s[ms], a[1]);
+      a[2] = __builtin_fmaf(q[2], s[ms], a[2]);
+      a[3] = __builtin_fmaf(q[3], s[ms], a[3]);
     }
   }
-}
-
-// Wait until this wave's DMA for the stage about to be read has landed (with
-// `later` younger stages still allowed in flight), then barrier so that every
-// wave's share has landed too.  lgkmcnt(0) also retires this wave's LDS reads
-// of the stage the next prefetch will overwrite.
-template <class C>
-__device__ __forceinline__ void wait_stage(int later) {
-  constexpr int L = C::kLoadsPerStage;
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (C::STAGES == 4) {
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<2 * L>::value);
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<L>::value);
-    else __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
-  } else if constexpr (C::STAGES == 3) {
-    if (later >= 1) __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<L>::value);
-    else __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
-  } else {
-    __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
+  if constexpr (C::kMfmas / kDmaGap < C::kLoadsPerStage) {
+#pragma unroll
+    for (int d = C::kMfmas / kDmaGap; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, d);
   }
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// One pipeline step for K block kb held in stage S; prefetches kb + STAGES - 1.
-template <class C, int S>
-__device__ __forceinline__ void step(const Tile<C>& t, f32x4 (&acc)[C::MS][C::NS], int kb, int kblocks,
-                                     int wr, int wc) {
-  // Stages issued after kb's and possibly still in flight: kb+1 .. kb+STAGES-2.
-  const int left = kblocks - 1 - kb;
-  wait_stage<C>(left < C::STAGES - 2 ? left : C::STAGES - 2);
-  constexpr int SN = (S + C::STAGES - 1) % C::STAGES;
-  if (kb + C::STAGES - 1 < kblocks) issue_stage<C, SN>(t, kb + C::STAGES - 1);
-  compute_stage<C, S>(acc, wr, wc);
+// One K block kb in LDS stage S = kb % kStages: wait for our DMA of kb (with 3
+// stages the group of kb+1 may stay in flight), barrier (every wave's DMA of kb
+// landed; every wave is done reading the stage kb-1 used), then compute kb while
+// the DMA of kb + kStages - 1 is issued into that freed stage.
+template <class C, int V, int S>
+__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], int kb, int kblocks,
+                                     int wave, int lane, uint32_t off0, uint32_t off1, int wr, int wc, int r16) {
+  // Every step issues one DMA group, so kStages - 2 younger groups may stay in flight.
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage>::value);
+  lds_barrier();
+  const int kbd = kb + C::kStages - 1;
+  compute_stage<C, V, S, (S + C::kStages - 1) % C::kStages>(acc, off0, off1, wr, wc, r16, t,
+                                                             kbd < kblocks ? kbd : kblocks - 1, wave, lane);
 }
-
-struct TileCoord {
-  int mt, nt, group;   // M tile (within the group for masked), N tile, group (or -1: skip)
-};
 
 __device__ __forceinline__ int remap_for_xcd(int b, int grid) {
   // Consecutive workgroup ids go to different XCDs (round-robin dispatch); give
@@ -236,15 +285,20 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& mt,
 
 template <class C, int V>
 __global__ void __launch_bounds__(C::kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(C::kWaves / 4, C::kWaves / 4)))
 gemm_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave / C::WAVES_N;
   const int wc = wave % C::WAVES_N;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
   const int kblocks = (int)(p.k / kKBlock);
   const int tiles_n = (int)((p.n + C::BN - 1) / C::BN);
   const int64_t n_sblocks = (p.n + 127) / 128;
+  // This lane's two 16-byte slots (logical slots 2q, 2q+1) inside any 16-row fragment.
+  const uint32_t off0 = r16 * kKBlock + (((2 * q) ^ swz16(r16)) << 4);
+  const uint32_t off1 = r16 * kKBlock + (((2 * q + 1) ^ swz16(r16)) << 4);
 
   // ---- tile space
   __shared__ int masked_prefix[V == kMasked ? kMaxMaskedGroups + 1 : 1];
@@ -288,7 +342,7 @@ gemm_kernel(GemmParams p) {
   for (int tile = remap_for_xcd(blockIdx.x, gridDim.x); tile < num_tiles; tile += gridDim.x) {
     // ---- decode the tile
     int mt, nt, g = 0;
-    int64_t m_limit = p.m;   // rows of A that exist (for clamping) / may be written
+    int64_t m_limit = p.m;   // rows that may be written
     if constexpr (V == kMasked) {
       // group: largest g with prefix[g] * tiles_n <= tile
       int lo = 0, hi = p.num_groups;          // invariant: prefix[lo]*tn <= tile < prefix[hi]*tn
@@ -313,42 +367,53 @@ gemm_kernel(GemmParams p) {
     }
     const int64_t m0 = (int64_t)mt * C::BM;
     const int64_t n0 = (int64_t)nt * C::BN;
-
-    const uint8_t* A = p.a + (V == kMasked ? (int64_t)g * p.a_gs : 0);
-    const float* SFA = p.sfa + (V == kMasked ? (int64_t)g * p.sfa_gs : 0);
-    const uint8_t* B = p.b + (V != kDense ? (int64_t)g * p.b_gs : 0);
-    const float* SFB = p.sfb + (V != kDense ? (int64_t)g * p.sfb_gs : 0);
     const int64_t a_rows = p.m;   // rows of A present in memory (per group when masked)
 
-    // ---- per-lane DMA sources at K block 0
-    Tile<C> t;
+    // Per-lane index math of this tile is done on a copy of the lane id that the
+    // compiler cannot see through, so that it is recomputed per tile instead of
+    // being hoisted out of the tile loop and kept live (or spilled) for the
+    // whole kernel.
+    int tl = lane;
+    asm volatile("" : "+v"(tl));
+
+    // ---- DMA sources: uniform bases, per-lane 32-bit offsets (host checks they fit)
+    TileSrc<C> t;
+    t.a_base = p.a + (V == kMasked ? (int64_t)g * p.a_gs : 0);
+    t.b_base = p.b + (V != kDense ? (int64_t)g * p.b_gs : 0);
 #pragma unroll
     for (int j = 0; j < C::kAChunksPerWave; ++j) {
-      const int prow = (wave * C::kAChunksPerWave + j) * 8 + (lane >> 3);
+      const int prow = (wave * C::kAChunksPerWave + j) * 8 + (tl >> 3);
       int64_t row = m0 + prow;
       row = row < a_rows ? row : a_rows - 1;
-      t.a_src[j] = A + row * p.lda + (((lane & 7) ^ swz(prow)) << 4);
+      t.a_off[j] = (uint32_t)(row * p.lda) + (((tl & 7) ^ swz16(prow)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < C::kBChunksPerWave; ++j) {
-      const int prow = (wave * C::kBChunksPerWave + j) * 8 + (lane >> 3);
+      // LDS row prow of the B stage holds, in fragment order, column
+      // n0 + wcol*WN + 4*NS*(fi/4) + 4*ft + fi%4 (ft = fragment, fi = row in it).
+      const int prow = (wave * C::kBChunksPerWave + j) * 8 + (tl >> 3);
       const int wcol = prow / C::WN;
       const int pl = prow % C::WN;
       const int ft = pl / 16, fi = pl % 16;
       int64_t col = n0 + wcol * C::WN + 4 * C::NS * (fi / 4) + 4 * ft + (fi % 4);
       col = col < p.n ? col : p.n - 1;
-      t.b_src[j] = B + col * p.ldb + (((lane & 7) ^ swz(prow)) << 4);
+      t.b_off[j] = (uint32_t)(col * p.ldb) + (((tl & 7) ^ swz16(prow)) << 4);
     }
-    if (lane < C::kSAPerWave) {
-      int64_t row = m0 + wave * C::kSAPerWave + lane;
-      row = row < a_rows ? row : a_rows - 1;
-      t.sa_src = SFA + row * p.sfa_sm;
-      t.s_kstride = p.sfa_sk;
-    } else {
-      int64_t nb = n0 / 128 + (lane - C::kSAPerWave);
-      nb = nb < n_sblocks ? nb : n_sblocks - 1;
-      t.sa_src = SFB + nb * p.sfb_sn;
-      t.s_kstride = p.sfb_sk;
+    {
+      const float* SFA = p.sfa + (V == kMasked ? (int64_t)g * p.sfa_gs : 0);
+      const float* SFB = p.sfb + (V != kDense ? (int64_t)g * p.sfb_gs : 0);
+      // every lane points at a valid scale (the DMA is unconditional); see kScaleFloats
+      if (tl < C::kSAPerWave) {
+        int64_t row = m0 + wave * C::kSAPerWave + tl;
+        row = row < a_rows ? row : a_rows - 1;
+        t.s_src = SFA + row * p.sfa_sm;
+        t.s_kstride = p.sfa_sk;
+      } else {
+        int64_t nb = n0 / 128 + (tl - C::kSAPerWave);
+        nb = nb < n_sblocks ? nb : n_sblocks - 1;
+        t.s_src = SFB + nb * p.sfb_sn;
+        t.s_kstride = p.sfb_sk;
+      }
     }
 
     f32x4 acc[C::MS][C::NS];
@@ -357,37 +422,35 @@ gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // ---- pipeline: all waves are done with the previous tile's stages here
+    // ---- prologue: every wave is done with the previous tile's LDS here
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_stage<C, 0>(t, 0);
-    if (C::STAGES >= 3 && 1 < kblocks) issue_stage<C, 1 % C::STAGES>(t, 1);
-    if (C::STAGES >= 4 && 2 < kblocks) issue_stage<C, 2 % C::STAGES>(t, 2);
+    lds_barrier();
+    issue_dma<C, V, 0>(t, 0, wave, lane);
+    if constexpr (C::kStages == 3) issue_dma<C, V, 1>(t, 1 < kblocks ? 1 : kblocks - 1, wave, lane);
 
-    for (int kb = 0; kb < kblocks; kb += C::STAGES) {
-      step<C, 0>(t, acc, kb, kblocks, wr, wc);
-      if (kb + 1 < kblocks) step<C, 1 % C::STAGES>(t, acc, kb + 1, kblocks, wr, wc);
-      if constexpr (C::STAGES >= 3)
-        if (kb + 2 < kblocks) step<C, 2 % C::STAGES>(t, acc, kb + 2, kblocks, wr, wc);
-      if constexpr (C::STAGES >= 4)
-        if (kb + 3 < kblocks) step<C, 3 % C::STAGES>(t, acc, kb + 3, kblocks, wr, wc);
+    // ---- main loop over K blocks, LDS stage = kb % kStages
+    int kb = 0;
+    for (; kb + C::kStages <= kblocks; kb += C::kStages) {
+      step<C, V, 0>(t, acc, kb + 0, kblocks, wave, lane, off0, off1, wr, wc, r16);
+      step<C, V, 1>(t, acc, kb + 1, kblocks, wave, lane, off0, off1, wr, wc, r16);
+      if constexpr (C::kStages == 3) step<C, V, 2 % C::kStages>(t, acc, kb + 2, kblocks, wave, lane, off0, off1, wr, wc, r16);
     }
+    if (kb < kblocks) step<C, V, 0>(t, acc, kb, kblocks, wave, lane, off0, off1, wr, wc, r16);
+    if (C::kStages == 3 && kb + 1 < kblocks) step<C, V, 1>(t, acc, kb + 1, kblocks, wave, lane, off0, off1, wr, wc, r16);
 
     // ---- epilogue: bf16 RNE, 16-byte stores of 8 consecutive columns
     uint16_t* D = p.d + (V == kMasked ? (int64_t)g * p.d_gs : 0);
-    const int r16 = lane & 15;
-    const int q = lane >> 4;
+    const int er16 = tl & 15, eq = tl >> 4;
 #pragma unroll
     for (int ms = 0; ms < C::MS; ++ms) {
-      const int64_t row = m0 + wr * C::WM + ms * 16 + r16;
+      const int64_t row = m0 + wr * C::WM + ms * 16 + er16;
       bool ok = row < m_limit;
       if constexpr (V == kContiguous) ok = ok && (p.m_indices[row] >= 0);
       if (!ok) continue;
       uint16_t* drow = D + row * p.ldd;
 #pragma unroll
       for (int j = 0; j < C::NS / 2; ++j) {
-        const int64_t col = n0 + wc * C::WN + 4 * C::NS * q + 8 * j;
+        const int64_t col = n0 + wc * C::WN + 4 * C::NS * eq + 8 * j;
         if (col < p.n) {
           const f32x4 x0 = acc[ms][2 * j];
           const f32x4 x1 = acc[ms][2 * j + 1];
@@ -401,10 +464,14 @@ gemm_kernel(GemmParams p) {
       }
     }
   }
+  // Tail steps re-issue the last K block's DMA into free stages: let them land
+  // before this workgroup's LDS can be handed to another one.
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
 }
 
-using CfgLarge = Cfg<128, 256, 2, 2, 3>;
-using CfgMid = Cfg<128, 128, 2, 2, 4>;
+using CfgHuge = Cfg<256, 256, 4, 2, 2, 1, 2>;
+using CfgLarge = Cfg<128, 256, 2, 4, 3>;
+using CfgMid = Cfg<128, 128, 2, 4, 3>;
 
 template <class C>
 hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stream) {
@@ -421,6 +488,7 @@ hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stre
 
 InstanceInfo instance_info(GemmInstance inst) {
   switch (inst) {
+    case kInstHuge: return {CfgHuge::BM, CfgHuge::BN};
     case kInstLarge: return {CfgLarge::BM, CfgLarge::BN};
     case kInstMid: return {CfgMid::BM, CfgMid::BN};
     default: return {0, 0};
@@ -429,6 +497,7 @@ InstanceInfo instance_info(GemmInstance inst) {
 
 hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int grid, hipStream_t stream) {
   switch (inst) {
+    case kInstHuge: return launch_cfg<CfgHuge>(v, p, grid, stream);
     case kInstLarge: return launch_cfg<CfgLarge>(v, p, grid, stream);
     case kInstMid: return launch_cfg<CfgMid>(v, p, grid, stream);
     default: return hipErrorInvalidValue;

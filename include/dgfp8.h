@@ -5,8 +5,15 @@
  * device address on the current HIP device; "stream" is a hipStream_t passed
  * as void* (NULL selects the default stream).  All work is enqueued on that
  * stream and the call returns without synchronising.  The caller owns every
- * buffer; the library allocates nothing per call and keeps no device state
- * besides the compute-unit count used for the persistent grid.
+ * input and output buffer.  Device state kept by the library, per device:
+ * the compute-unit count used for the persistent grid and, from the first
+ * dense GEMM that splits its K range (small M, see dg_fp8_gemm_nt), a 64 MiB
+ * fp32 workspace plus 256 KiB of arrival counters.  That workspace is
+ * allocated (hipMalloc, then a synchronous clear) inside that first call and
+ * kept until the process ends, so make the first small-M dense call outside
+ * HIP graph capture.  Split-K calls on one device share the workspace: two
+ * of them running at the same time (different streams) race; calls on one
+ * stream are ordered and safe.
  *
  * Errors: every entry point validates its arguments on the host and returns a
  * dg_status.  Nothing aborts and no exception crosses the ABI.  A problem
@@ -65,6 +72,11 @@ const char* dg_status_string(dg_status status);
  *   b   device, E4M3 [n, k], row stride ldb
  *   sfb device, fp32 [ceil(n/128), k/128] with strides sfb_sn, sfb_sk
  *   d   device, bf16 [m, n], row stride ldd (elements); fully overwritten
+ * When the output has too few tiles to occupy the device (small m), the K
+ * blocks are split over several workgroups per output tile: each sums its
+ * K blocks in order into an fp32 partial, and the partials are added in split
+ * order, so results are deterministic run to run (and independent of
+ * dg_set_num_cus) but may differ from the unsplit sum in the last fp32 bits.
  * Page "GitHub 推荐…DeepGEMM…", 解法哲学 (fp8_gemm_nt with output d);
  * page juejin.cn, section 4(3) (dense GEMM type).
  */
@@ -181,6 +193,14 @@ int dg_get_mk_alignment_for_contiguous_layout(void);
  */
 dg_status dg_set_num_cus(int num_cus);
 int dg_get_num_cus(void);
+
+/*
+ * Enables (non-zero, the default) or disables the split-K path of
+ * dg_fp8_gemm_nt; returns the previous setting.  Disabling it trades small-M
+ * speed for a library that never allocates.  The two paths agree to fp32
+ * rounding of the K-block partial sums, not bit for bit.
+ */
+int dg_set_split_k(int enable);
 
 #ifdef __cplusplus
 }

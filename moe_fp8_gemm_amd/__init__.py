@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdgfp8.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_fp8_gemm_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python moe_fp8_gemm_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -45,6 +45,7 @@ _SIGNATURES = {
     "dg_get_mk_alignment_for_contiguous_layout": ([], _i32),
     "dg_set_num_cus": ([_i32], _i32),
     "dg_get_num_cus": ([], _i32),
+    "dg_set_split_k": ([_i32], _i32),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -203,3 +204,8 @@ def set_num_cus(num_cus: int) -> None:
 
 def get_num_cus() -> int:
     return lib.dg_get_num_cus()
+
+
+def set_split_k(enable: bool) -> bool:
+    """Enable or disable the split-K path of fp8_gemm_nt; returns the previous setting."""
+    return bool(lib.dg_set_split_k(int(bool(enable))))

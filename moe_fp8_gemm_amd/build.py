@@ -1,6 +1,8 @@
 """Build libdgfp8.so in-tree with hipcc for gfx950.
 
-    python -m moe_fp8_gemm_amd.build [-v]
+    python moe_fp8_gemm_amd/build.py [-v]
+
+(run it as a script: importing the package loads the library being built)
 
 Every HIP source is compiled with packed-fp32 code generation disabled and the
 default (correctly rounded) fp32 division; no fast-math flags.

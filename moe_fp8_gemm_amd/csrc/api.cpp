@@ -19,10 +19,11 @@ constexpr int kMaxMaskedGroups = 1024;
 constexpr int kMaxDevices = 64;
 
 int g_num_cus_override = 0;
+int g_split_k_enabled = 1;
 int g_device_cus[kMaxDevices] = {0};
 
-int device_cus() {
-  if (g_num_cus_override > 0) return g_num_cus_override;
+// Compute units of the current device (ignores the override).
+int hw_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   if (g_device_cus[dev] == 0) {
@@ -32,6 +33,9 @@ int device_cus() {
   }
   return g_device_cus[dev];
 }
+
+// Width of the persistent grid.
+int device_cus() { return g_num_cus_override > 0 ? g_num_cus_override : hw_cus(); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -71,6 +75,112 @@ GemmInstance choose_dense(int64_t m, int64_t n, int cus) {
   for (GemmInstance inst : {kInstLarge, kInstHuge}) {
     const double c = instance_cost(inst, m, 0, n, cus);
     if (c < best_cost) { best = inst; best_cost = c; }
+  }
+  return best;
+}
+
+// ---- split-K for small M (too few output tiles to keep the CUs streaming B)
+
+constexpr int64_t kSplitWsBytes = 64ll << 20;   // fp32 partial tiles
+constexpr int kSplitCounters = 1 << 16;         // arrival counters (one per output tile)
+
+struct SplitWorkspace {
+  float* ws = nullptr;
+  int* counters = nullptr;
+};
+SplitWorkspace g_split_ws[kMaxDevices];
+
+// Allocated on a device's first split-K call and kept for the process lifetime;
+// the counters start at zero and every kernel leaves them at zero.
+dg_status split_workspace(SplitWorkspace*& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DG_ERROR_LAUNCH;
+  SplitWorkspace& w = g_split_ws[dev];
+  if (!w.ws) {
+    void* ws = nullptr;
+    void* cnt = nullptr;
+    if (hipMalloc(&ws, kSplitWsBytes) != hipSuccess) return DG_ERROR_LAUNCH;
+    if (hipMalloc(&cnt, kSplitCounters * sizeof(int)) != hipSuccess ||
+        hipMemset(cnt, 0, kSplitCounters * sizeof(int)) != hipSuccess) {
+      (void)hipFree(ws);
+      if (cnt) (void)hipFree(cnt);
+      return DG_ERROR_LAUNCH;
+    }
+    w.ws = static_cast<float*>(ws);
+    w.counters = static_cast<int*>(cnt);
+  }
+  out = &w;
+  return DG_SUCCESS;
+}
+
+struct DensePlan {
+  GemmInstance inst;
+  int64_t tiles;      // output tiles
+  int splits;         // 1: plain dense kernel
+  int kb_per_split;
+};
+
+DensePlan make_plan(GemmInstance inst, int64_t m, int64_t n, int64_t kblocks, int64_t splits) {
+  const InstanceInfo info = instance_info(inst);
+  DensePlan plan{inst, ceil_div(m, info.bm) * ceil_div(n, info.bn), 1, (int)kblocks};
+  if (splits > 1) {
+    plan.kb_per_split = (int)ceil_div(kblocks, splits);
+    plan.splits = (int)ceil_div(kblocks, plan.kb_per_split);
+  }
+  return plan;
+}
+
+// Estimated time of a small-M plan (seconds).  Every unit (output tile, or its
+// share of K when split) pays a start-up cost, then a per-K-block cost of its
+// instance; a split unit also publishes an fp32 partial tile, and the last unit
+// of each tile reads all of them back.  Units run in rounds of one per CU.  The
+// constants are fitted to MI355X timings of the dense LLM-layer shapes with
+// M in {64, 128, 256}, operands in HBM; the plans they pick are within a few
+// percent of the best measured plan on each of those shapes.
+double plan_seconds(const DensePlan& pl, int cus) {
+  constexpr double kUnitStart = 4.3e-6;
+  constexpr double kReduceBytesPerSec = 27.6e9;
+  double per_kb = 0.0, split_cost = 0.0;
+  switch (pl.inst) {
+    case kInstSkinny64: per_kb = 0.54e-6; split_cost = 1.6e-6; break;
+    case kInstSkinny128: per_kb = 0.69e-6; split_cost = 0.7e-6; break;
+    case kInstMid: per_kb = 0.89e-6; split_cost = 0.0; break;
+    case kInstLarge: per_kb = 1.06e-6; split_cost = 80e-6; break;   // never worth splitting
+    default: per_kb = 2.0e-6; split_cost = 80e-6; break;
+  }
+  const InstanceInfo info = instance_info(pl.inst);
+  const int64_t units = pl.tiles * pl.splits;
+  const double rounds = (double)ceil_div(units, cus);
+  const double unit = kUnitStart + pl.kb_per_split * per_kb + (pl.splits > 1 ? split_cost : 0.0);
+  double t = rounds * unit;
+  if (pl.splits > 1) t += pl.splits * (double)info.bm * info.bn * 4 / kReduceBytesPerSec;
+  return t;
+}
+
+constexpr int kMinKbPerSplit = 2;   // at least 256 of K per unit
+
+// Dense plan: the plain instance choice, unless it leaves more than half of the
+// CUs idle; then the cheapest (instance, split) pair by plan_seconds (the CU
+// count is a parameter so that the plan, and with it the summation order, does
+// not depend on the grid-width override).
+DensePlan plan_dense(int64_t m, int64_t n, int64_t k, int cus, bool allow_split) {
+  const int64_t kblocks = k / 128;
+  const DensePlan plain = make_plan(choose_dense(m, n, cus), m, n, kblocks, 1);
+  if (plain.tiles * 2 > cus) return plain;
+  DensePlan best = plain;
+  double best_t = plan_seconds(plain, cus);
+  for (GemmInstance inst : {kInstSkinny64, kInstSkinny128, kInstMid, kInstLarge}) {
+    const InstanceInfo info = instance_info(inst);
+    if (inst == kInstSkinny64 && m > 64) continue;
+    const int64_t tiles = ceil_div(m, info.bm) * ceil_div(n, info.bn);
+    const int64_t max_splits = allow_split && tiles <= kSplitCounters ? kblocks / kMinKbPerSplit : 1;
+    for (int64_t s = 1; s <= max_splits || s == 1; ++s) {
+      if (s > 1 && tiles * s * info.bm * info.bn * (int64_t)sizeof(float) > kSplitWsBytes) break;
+      const DensePlan pl = make_plan(inst, m, n, kblocks, s);
+      if (pl.splits != s && s > 1) continue;   // same as a smaller split count
+      const double t = plan_seconds(pl, cus);
+      if (t < best_t) { best = pl; best_t = t; }
+    }
   }
   return best;
 }
@@ -126,10 +236,20 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
   p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
-  const GemmInstance inst = choose_dense(m, n, device_cus());
-  const InstanceInfo info = instance_info(inst);
-  const int64_t tiles = ceil_div(m, info.bm) * ceil_div(n, info.bn);
-  return launch(inst, kDense, p, tiles, static_cast<hipStream_t>(stream));
+  // The plan (and so the summation order) follows the hardware CU count, never
+  // the grid-width override, so results do not depend on the override.
+  const DensePlan plan = plan_dense(m, n, k, hw_cus(), g_split_k_enabled != 0);
+  if (plan.splits > 1) {
+    SplitWorkspace* w = nullptr;
+    const dg_status ws_st = split_workspace(w);
+    if (ws_st != DG_SUCCESS) return ws_st;
+    p.ws = w->ws;
+    p.counters = w->counters;
+    p.splits = plan.splits;
+    p.kb_per_split = plan.kb_per_split;
+    return launch(plan.inst, kDenseSplitK, p, plan.tiles * plan.splits, static_cast<hipStream_t>(stream));
+  }
+  return launch(plan.inst, kDense, p, plan.tiles, static_cast<hipStream_t>(stream));
 }
 
 DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
@@ -253,3 +373,9 @@ DG_EXPORT dg_status dg_set_num_cus(int num_cus) {
 }
 
 DG_EXPORT int dg_get_num_cus(void) { return device_cus(); }
+
+DG_EXPORT int dg_set_split_k(int enable) {
+  const int prev = g_split_k_enabled;
+  g_split_k_enabled = enable ? 1 : 0;
+  return prev;
+}

@@ -8,7 +8,9 @@
 
 namespace dgfp8 {
 
-enum Variant : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kDenseSplitK: dense GEMM whose K range is split over several workgroups per
+// output tile (small M); partial sums go through a workspace.
+enum Variant : int { kDense = 0, kContiguous = 1, kMasked = 2, kDenseSplitK = 3 };
 
 // Everything a GEMM launch needs.  Pointers are device addresses; strides are
 // in elements (bytes for the E4M3 operands).
@@ -28,6 +30,12 @@ struct GemmParams {
   int64_t m;                      // dense: M, contiguous: m_total, masked: max_m
   int64_t n, k;
   int num_groups;
+  // split-K only: fp32 partial tiles [tiles][splits][BM*BN] and one arrival
+  // counter per output tile (zero on entry, left zero on exit)
+  float* ws;
+  int* counters;
+  int splits;
+  int kb_per_split;
 };
 
 // Kernel instances the host can pick (see gemm_fp8.hip for the tile shapes).
@@ -35,6 +43,8 @@ enum GemmInstance : int {
   kInstLarge = 0,     // 128 x 256 output tiles, 8 waves, 3-stage LDS pipeline
   kInstMid = 1,       // 128 x 128 output tiles, 8 waves, 3-stage LDS pipeline
   kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
+  kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves (small M, usually split over K)
+  kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves (M <= 64, usually split over K)
   kNumInstances
 };
 

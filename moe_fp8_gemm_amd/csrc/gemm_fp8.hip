@@ -116,7 +116,8 @@ struct Cfg {
   static_assert(kSAPerWave + kNSB <= 64, "scale DMA of the last wave");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one 128-column scale block");
   static_assert(NS % 2 == 0, "epilogue stores 8 columns at a time");
-  static_assert(kStages == 2 || kStages == 3, "pipeline depth");
+  static_assert(kStages >= 2 && kStages <= 8, "pipeline depth");
+  static_assert((kStages - 2) * kLoadsPerStage <= 63, "vmcnt range of the stage wait");
 };
 
 // LDS buffers, one variable per (config, variant, stage, kind): every kernel owns
@@ -336,12 +337,12 @@ gemm_kernel(GemmParams p) {
     num_tiles = masked_prefix[kMaxMaskedGroups] * tiles_n;
   } else {
     tiles_m = (int)((p.m + C::BM - 1) / C::BM);
-    num_tiles = tiles_m * tiles_n;
+    num_tiles = tiles_m * tiles_n * (V == kDenseSplitK ? p.splits : 1);
   }
 
   for (int tile = remap_for_xcd(blockIdx.x, gridDim.x); tile < num_tiles; tile += gridDim.x) {
     // ---- decode the tile
-    int mt, nt, g = 0;
+    int mt, nt, g = 0, split = 0;
     int64_t m_limit = p.m;   // rows that may be written
     if constexpr (V == kMasked) {
       // group: largest g with prefix[g] * tiles_n <= tile
@@ -358,6 +359,10 @@ gemm_kernel(GemmParams p) {
       int mm = p.masked_m[g];
       mm = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
       m_limit = mm;
+    } else if constexpr (V == kDenseSplitK) {
+      // consecutive units are the splits of one output tile: they run together
+      split = tile % p.splits;
+      raster(tile / p.splits, tiles_m, tiles_n, mt, nt);
     } else {
       raster(tile, tiles_m, tiles_n, mt, nt);
       if constexpr (V == kContiguous) {
@@ -402,18 +407,31 @@ gemm_kernel(GemmParams p) {
     {
       const float* SFA = p.sfa + (V == kMasked ? (int64_t)g * p.sfa_gs : 0);
       const float* SFB = p.sfb + (V != kDense ? (int64_t)g * p.sfb_gs : 0);
-      // every lane points at a valid scale (the DMA is unconditional); see kScaleFloats
-      if (tl < C::kSAPerWave) {
-        int64_t row = m0 + wave * C::kSAPerWave + tl;
-        row = row < a_rows ? row : a_rows - 1;
-        t.s_src = SFA + row * p.sfa_sm;
-        t.s_kstride = p.sfa_sk;
-      } else {
-        int64_t nb = n0 / 128 + (tl - C::kSAPerWave);
+      // Every lane points at a valid scale (the DMA is unconditional; see
+      // kScaleFloats).  Lanes whose slot is not used repeat the address of the
+      // wave's first A row, so that the load touches no cache line beyond those
+      // holding the scales the tile needs.
+      const int j = tl - C::kSAPerWave;
+      if (wave == C::kWaves - 1 && j >= 0 && j < C::kNSB) {
+        int64_t nb = n0 / 128 + j;
         nb = nb < n_sblocks ? nb : n_sblocks - 1;
         t.s_src = SFB + nb * p.sfb_sn;
         t.s_kstride = p.sfb_sk;
+      } else {
+        int64_t row = m0 + wave * C::kSAPerWave + (tl < C::kSAPerWave ? tl : 0);
+        row = row < a_rows ? row : a_rows - 1;
+        t.s_src = SFA + row * p.sfa_sm;
+        t.s_kstride = p.sfa_sk;
       }
+    }
+
+    int kbs = kblocks;   // K blocks of this unit
+    if constexpr (V == kDenseSplitK) {
+      const int kb0 = split * p.kb_per_split;
+      kbs = min(p.kb_per_split, kblocks - kb0);
+      t.a_base += (int64_t)kb0 * kKBlock;
+      t.b_base += (int64_t)kb0 * kKBlock;
+      t.s_src += (int64_t)kb0 * t.s_kstride;
     }
 
     f32x4 acc[C::MS][C::NS];
@@ -425,22 +443,79 @@ gemm_kernel(GemmParams p) {
     // ---- prologue: every wave is done with the previous tile's LDS here
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
     lds_barrier();
-    issue_dma<C, V, 0>(t, 0, wave, lane);
-    if constexpr (C::kStages == 3) issue_dma<C, V, 1>(t, 1 < kblocks ? 1 : kblocks - 1, wave, lane);
+    // K blocks 0 .. kStages-2 into stages 0 .. kStages-2 (the last block again
+    // where the unit has fewer)
+#define DG_PROLOGUE(I) \
+    if constexpr (I < C::kStages - 1) issue_dma<C, V, I>(t, I < kbs ? I : kbs - 1, wave, lane);
+    DG_PROLOGUE(0) DG_PROLOGUE(1) DG_PROLOGUE(2) DG_PROLOGUE(3) DG_PROLOGUE(4) DG_PROLOGUE(5) DG_PROLOGUE(6)
+#undef DG_PROLOGUE
 
-    // ---- main loop over K blocks, LDS stage = kb % kStages
+    // ---- main loop over K blocks, LDS stage = kb % kStages: whole periods of
+    // kStages blocks, then the remaining kbs % kStages blocks
     int kb = 0;
-    for (; kb + C::kStages <= kblocks; kb += C::kStages) {
-      step<C, V, 0>(t, acc, kb + 0, kblocks, wave, lane, off0, off1, wr, wc, r16);
-      step<C, V, 1>(t, acc, kb + 1, kblocks, wave, lane, off0, off1, wr, wc, r16);
-      if constexpr (C::kStages == 3) step<C, V, 2 % C::kStages>(t, acc, kb + 2, kblocks, wave, lane, off0, off1, wr, wc, r16);
+#define DG_STEP(I) \
+    if constexpr (I < C::kStages) step<C, V, I>(t, acc, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+    for (; kb + C::kStages <= kbs; kb += C::kStages) {
+      DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
     }
-    if (kb < kblocks) step<C, V, 0>(t, acc, kb, kblocks, wave, lane, off0, off1, wr, wc, r16);
-    if (C::kStages == 3 && kb + 1 < kblocks) step<C, V, 1>(t, acc, kb + 1, kblocks, wave, lane, off0, off1, wr, wc, r16);
+#undef DG_STEP
+#define DG_TAIL(I)                     \
+    if constexpr (I < C::kStages - 1) \
+      if (kb + I < kbs) step<C, V, I>(t, acc, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+    DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
+#undef DG_TAIL
 
     // ---- epilogue: bf16 RNE, 16-byte stores of 8 consecutive columns
     uint16_t* D = p.d + (V == kMasked ? (int64_t)g * p.d_gs : 0);
     const int er16 = tl & 15, eq = tl >> 4;
+    if constexpr (V == kDenseSplitK) {
+      // Publish this unit's partial tile, count arrivals; the last unit of the
+      // output tile adds all partials in split order (deterministic whatever the
+      // arrival order) and writes D.  Partials are kept in register order, not
+      // as a matrix: element c of acc[ms][j] of lane l of wave w sits at
+      // ((w * MS * NS + ms * NS + j) * 4 + c) * 64 + l, so that every store and
+      // load instruction covers 256 contiguous bytes.  The units of one tile may
+      // run on different XCDs, whose L2 caches are not coherent with each other
+      // for plain accesses: the partials move by device-scope relaxed atomic
+      // stores and loads (written through to / read from the device-coherent
+      // level), which avoids the L2-wide writeback and invalidate that a
+      // device-scope fence costs.
+      const int tile_mn = mt * tiles_n + nt;
+      float* part = p.ws + (int64_t)tile_mn * p.splits * (C::BM * C::BN) + wave * (C::kMfmas * 256) + tl;
+#pragma unroll
+      for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+        for (int j = 0; j < C::NS; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            __hip_atomic_store(part + (int64_t)split * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
+                               acc[ms][j][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every partial store has been acknowledged before the arrival is counted
+      __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
+      __shared__ int last_flag;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        last_flag = __hip_atomic_fetch_add(p.counters + tile_mn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    p.splits - 1;
+      __syncthreads();
+      if (!last_flag) continue;
+#pragma unroll
+      for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+        for (int j = 0; j < C::NS; ++j) acc[ms][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < p.splits; ++sp) {
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+          for (int j = 0; j < C::NS; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              acc[ms][j][c] += __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // ready for the next call
+      if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
     for (int ms = 0; ms < C::MS; ++ms) {
       const int64_t row = m0 + wr * C::WM + ms * 16 + er16;
@@ -470,25 +545,45 @@ gemm_kernel(GemmParams p) {
 }
 
 using CfgHuge = Cfg<256, 256, 4, 2, 2, 1, 2>;
+using CfgSkinny128 = Cfg<128, 64, 4, 2, 3>;
+using CfgSkinny64 = Cfg<64, 64, 4, 2, 3>;
 using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
 
-template <class C>
+// Variants compiled per configuration: bit v of Mask set = variant v available.
+template <class C, int Mask>
 hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stream) {
   dim3 block(C::kThreads);
+  if (!((Mask >> v) & 1)) return hipErrorInvalidValue;
   switch (v) {
-    case kDense: hipLaunchKernelGGL((gemm_kernel<C, kDense>), dim3(grid), block, 0, stream, p); break;
-    case kContiguous: hipLaunchKernelGGL((gemm_kernel<C, kContiguous>), dim3(grid), block, 0, stream, p); break;
-    case kMasked: hipLaunchKernelGGL((gemm_kernel<C, kMasked>), dim3(grid), block, 0, stream, p); break;
+    case kDense:
+      if constexpr ((Mask >> kDense) & 1) hipLaunchKernelGGL((gemm_kernel<C, kDense>), dim3(grid), block, 0, stream, p);
+      break;
+    case kContiguous:
+      if constexpr ((Mask >> kContiguous) & 1)
+        hipLaunchKernelGGL((gemm_kernel<C, kContiguous>), dim3(grid), block, 0, stream, p);
+      break;
+    case kMasked:
+      if constexpr ((Mask >> kMasked) & 1) hipLaunchKernelGGL((gemm_kernel<C, kMasked>), dim3(grid), block, 0, stream, p);
+      break;
+    case kDenseSplitK:
+      if constexpr ((Mask >> kDenseSplitK) & 1)
+        hipLaunchKernelGGL((gemm_kernel<C, kDenseSplitK>), dim3(grid), block, 0, stream, p);
+      break;
   }
   return hipGetLastError();
 }
+
+constexpr int kAll = (1 << kDense) | (1 << kContiguous) | (1 << kMasked) | (1 << kDenseSplitK);
+constexpr int kDenseAndSplit = (1 << kDense) | (1 << kDenseSplitK);
 
 }  // namespace
 
 InstanceInfo instance_info(GemmInstance inst) {
   switch (inst) {
     case kInstHuge: return {CfgHuge::BM, CfgHuge::BN};
+    case kInstSkinny128: return {CfgSkinny128::BM, CfgSkinny128::BN};
+    case kInstSkinny64: return {CfgSkinny64::BM, CfgSkinny64::BN};
     case kInstLarge: return {CfgLarge::BM, CfgLarge::BN};
     case kInstMid: return {CfgMid::BM, CfgMid::BN};
     default: return {0, 0};
@@ -497,9 +592,11 @@ InstanceInfo instance_info(GemmInstance inst) {
 
 hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int grid, hipStream_t stream) {
   switch (inst) {
-    case kInstHuge: return launch_cfg<CfgHuge>(v, p, grid, stream);
-    case kInstLarge: return launch_cfg<CfgLarge>(v, p, grid, stream);
-    case kInstMid: return launch_cfg<CfgMid>(v, p, grid, stream);
+    case kInstHuge: return launch_cfg<CfgHuge, (1 << kDense) | (1 << kMasked)>(v, p, grid, stream);
+    case kInstSkinny128: return launch_cfg<CfgSkinny128, kDenseAndSplit>(v, p, grid, stream);
+    case kInstSkinny64: return launch_cfg<CfgSkinny64, kDenseAndSplit>(v, p, grid, stream);
+    case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);
+    case kInstMid: return launch_cfg<CfgMid, kAll>(v, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -89,8 +89,9 @@ def test_power_of_two_scale_linearity_bit_exact():
     assert np.array_equal(f(down), f(base) * np.float32(0.25))
 
 
-def test_deterministic_and_independent_of_grid_width():
-    qa, sa, qb, sb = _host_problem(700, 1032, 768, seed=8)
+@pytest.mark.parametrize("m,n,k", [(700, 1032, 768), (96, 1032, 3072)])
+def test_deterministic_and_independent_of_grid_width(m, n, k):
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=8)
     ref = _gpu_dense(qa, sa, qb, sb)
     assert np.array_equal(ref, _gpu_dense(qa, sa, qb, sb))
     try:
@@ -100,7 +101,46 @@ def test_deterministic_and_independent_of_grid_width():
             assert np.array_equal(ref, _gpu_dense(qa, sa, qb, sb)), cus
     finally:
         dg.set_num_cus(0)
-    assert_gemm_close(ref, ogemm.gemm_nt(qa, sa, qb, sb), "700x1032x768")
+    assert_gemm_close(ref, ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
+
+
+# Small M with deep K: the output has too few tiles for the device, so the K
+# blocks are split over several workgroups per output tile (partials summed in
+# split order by the last one to arrive).
+SPLIT = [(1, 8, 1024), (16, 1536, 2048), (64, 520, 4096), (65, 8, 640), (100, 264, 1024),
+         (128, 2112, 1536), (129, 264, 1536), (77, 136, 1280)]
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT)
+def test_split_k_parity_and_agreement(m, n, k):
+    print(f"split-K {m}x{n}x{k}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m * 11 + n * 5 + k)
+    want = ogemm.gemm_nt(qa, sa, qb, sb)
+    split = _gpu_dense(qa, sa, qb, sb)
+    assert_gemm_close(split, want, f"split {m}x{n}x{k}")
+    # a second call reuses the workspace and its (reset) arrival counters
+    assert np.array_equal(split, _gpu_dense(qa, sa, qb, sb))
+    prev = dg.set_split_k(False)
+    try:
+        plain = _gpu_dense(qa, sa, qb, sb)
+    finally:
+        dg.set_split_k(prev)
+    assert_gemm_close(plain, want, f"unsplit {m}x{n}x{k}")
+
+
+def test_split_k_consecutive_problems_share_the_workspace():
+    """Back-to-back calls of different shapes on one stream, no host sync between."""
+    probs = [_host_problem(m, n, k, seed=40 + i)
+             for i, (m, n, k) in enumerate([(64, 1032, 2048), (120, 264, 4096), (8, 2048, 1024)])]
+    outs = []
+    for qa, sa, qb, sb in probs:
+        m, n = qa.shape[0], qb.shape[0]
+        d = sentinel_like((m, n))
+        dg.fp8_gemm_nt((upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb)), d)
+        outs.append(d)
+    torch.cuda.synchronize()
+    for (qa, sa, qb, sb), d in zip(probs, outs):
+        assert_gemm_close(bits(d), ogemm.gemm_nt(qa, sa, qb, sb), f"{qa.shape[0]}x{qb.shape[0]}")
 
 
 # ------------------------------------------------------------------ full size, sampled

@@ -53,14 +53,17 @@ def make_dense(dg, m, n, k, seed, dev):
 
 
 class Flusher:
-    """Overwrites a buffer larger than the MALL so that cold-cache timings do not
-    see operands left in the 256 MB Infinity Cache."""
+    """Reads a 1 GiB buffer so that cold-cache timings do not see operands left in
+    the 256 MB Infinity Cache (MALL) or the L2s.  It reads rather than writes: a
+    write flush leaves the MALL full of dirty lines whose write-back would then
+    be charged to the timed kernel."""
 
     def __init__(self, dev, nbytes=1 << 30):
-        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def __call__(self):
-        self.buf.fill_(1.0)
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def event_time_ms(fn, reps, flush=None):

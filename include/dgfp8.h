@@ -5,15 +5,9 @@
  * device address on the current HIP device; "stream" is a hipStream_t passed
  * as void* (NULL selects the default stream).  All work is enqueued on that
  * stream and the call returns without synchronising.  The caller owns every
- * input and output buffer.  Device state kept by the library, per device:
- * the compute-unit count used for the persistent grid and, from the first
- * dense GEMM that splits its K range (small M, see dg_fp8_gemm_nt), a 64 MiB
- * fp32 workspace plus 256 KiB of arrival counters.  That workspace is
- * allocated (hipMalloc, then a synchronous clear) inside that first call and
- * kept until the process ends, so make the first small-M dense call outside
- * HIP graph capture.  Split-K calls on one device share the workspace: two
- * of them running at the same time (different streams) race; calls on one
- * stream are ordered and safe.
+ * buffer, including the optional split-K workspace of dg_fp8_gemm_nt_ws; the
+ * library allocates no device memory and keeps no device state besides the
+ * compute-unit count used for the persistent grid.
  *
  * Errors: every entry point validates its arguments on the host and returns a
  * dg_status.  Nothing aborts and no exception crosses the ABI.  A problem
@@ -72,11 +66,8 @@ const char* dg_status_string(dg_status status);
  *   b   device, E4M3 [n, k], row stride ldb
  *   sfb device, fp32 [ceil(n/128), k/128] with strides sfb_sn, sfb_sk
  *   d   device, bf16 [m, n], row stride ldd (elements); fully overwritten
- * When the output has too few tiles to occupy the device (small m), the K
- * blocks are split over several workgroups per output tile: each sums its
- * K blocks in order into an fp32 partial, and the partials are added in split
- * order, so results are deterministic run to run (and independent of
- * dg_set_num_cus) but may differ from the unsplit sum in the last fp32 bits.
+ * Never splits the K range (see dg_fp8_gemm_nt_ws); equivalent to
+ * dg_fp8_gemm_nt_ws with no workspace.
  * Page "GitHub 推荐…DeepGEMM…", 解法哲学 (fp8_gemm_nt with output d);
  * page juejin.cn, section 4(3) (dense GEMM type).
  */
@@ -87,6 +78,40 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda,
                          void* d, int64_t ldd,
                          int64_t m, int64_t n, int64_t k,
                          void* stream);
+
+/*
+ * Dense GEMM as dg_fp8_gemm_nt, with a caller-provided workspace that lets a
+ * small-m problem (too few output tiles to occupy the device) split its K
+ * blocks over several workgroups per output tile.  Each split unit sums its
+ * K blocks in order into an fp32 partial tile; the last unit to finish adds
+ * the partials in split order and writes D.  Results are deterministic and
+ * independent of dg_set_num_cus, but may differ from the unsplit sum in the
+ * last fp32 bits (both within the method's tolerance).
+ *   ws        device, 16-byte aligned, ws_bytes long, or NULL (no split).
+ *             Its first 256 KiB hold arrival counters: they must be zero
+ *             before the workspace is first used, and every completed call
+ *             leaves them zero, so a workspace can be reused by any later call
+ *             on the same stream.  Calls that may run concurrently need
+ *             distinct workspaces.  The rest holds fp32 partial tiles.
+ *   ws_bytes  at least dg_fp8_gemm_nt_workspace_size(m, n, k) to enable the
+ *             split; a smaller (or NULL) workspace runs the unsplit kernel.
+ * Split-K is this library's answer to small m on a 256-CU device; the pages
+ * only note that thin shapes (small M, large N and K) run at low efficiency
+ * (page discosf.com news post on DeepGEMM, sections 4.3 and 5.4).
+ */
+dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda,
+                            const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                            const void* b, int64_t ldb,
+                            const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                            void* d, int64_t ldd,
+                            int64_t m, int64_t n, int64_t k,
+                            void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace bytes dg_fp8_gemm_nt_ws needs to split this problem; 0 when the
+ * problem runs unsplit (or the sizes are invalid).  Depends only on m, n, k
+ * and the device's compute-unit count. */
+size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /*
  * M-grouped GEMM, contiguous layout (MoE prefill / training forward).
@@ -193,14 +218,6 @@ int dg_get_mk_alignment_for_contiguous_layout(void);
  */
 dg_status dg_set_num_cus(int num_cus);
 int dg_get_num_cus(void);
-
-/*
- * Enables (non-zero, the default) or disables the split-K path of
- * dg_fp8_gemm_nt; returns the previous setting.  Disabling it trades small-M
- * speed for a library that never allocates.  The two paths agree to fp32
- * rounding of the K-block partial sums, not bit for bit.
- */
-int dg_set_split_k(int enable);
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,9 @@ _SIGNATURES = {
     "dg_get_mk_alignment_for_contiguous_layout": ([], _i32),
     "dg_set_num_cus": ([_i32], _i32),
     "dg_get_num_cus": ([], _i32),
-    "dg_set_split_k": ([_i32], _i32),
+    "dg_fp8_gemm_nt_ws": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
+                           _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "dg_fp8_gemm_nt_workspace_size": ([_i64, _i64, _i64], ctypes.c_size_t),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -96,12 +98,35 @@ def _out_bf16(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+_AUTO = "auto"
+_workspaces = {}
+
+
+def workspace_size(m: int, n: int, k: int) -> int:
+    """Bytes of split-K workspace fp8_gemm_nt can use for this problem (0: never splits)."""
+    return int(lib.dg_fp8_gemm_nt_workspace_size(int(m), int(n), int(k)))
+
+
+def _auto_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    # One zero-filled workspace per device, grown on demand.  Calls leave its
+    # counter block zero, so it is reused by every later call; calls that may run
+    # concurrently on different streams must pass their own workspaces.
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[idx] = ws
+    return ws
+
+
 def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
-                d: torch.Tensor) -> torch.Tensor:
+                d: torch.Tensor, workspace=_AUTO) -> torch.Tensor:
     """d[m, n] = bf16( A . B^T ) with per-(row, 128-K) A scales and per-128x128 B scales.
 
     a = (codes [m, k], sfa [m, k/128]); b = (codes [n, k], sfb [ceil(n/128), k/128]);
-    d bf16 [m, n] is overwritten and returned.
+    d bf16 [m, n] is overwritten and returned.  ``workspace``: "auto" (a cached
+    per-device buffer, enabling split-K for small m), None (never split), or a
+    zero-initialised uint8 device tensor of at least ``workspace_size(m, n, k)`` bytes.
     """
     (qa, sa), (qb, sb) = a, b
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
@@ -109,9 +134,20 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
     n = qb.shape[0]
     if qb.shape[1] != k or d.shape != (m, n):
         raise ValueError("shape mismatch")
-    _check(lib.dg_fp8_gemm_nt(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
-                              qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
-                              d.data_ptr(), d.stride(0), m, n, k, _stream()), "dg_fp8_gemm_nt")
+    if isinstance(workspace, str):
+        if workspace != _AUTO:
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = workspace_size(m, n, k)
+        workspace = _auto_workspace(d.device, need) if need > 0 else None
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.dg_fp8_gemm_nt_ws(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+                                 qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
+                                 d.data_ptr(), d.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream()),
+           "dg_fp8_gemm_nt")
     return d
 
 
@@ -205,7 +241,3 @@ def set_num_cus(num_cus: int) -> None:
 def get_num_cus() -> int:
     return lib.dg_get_num_cus()
 
-
-def set_split_k(enable: bool) -> bool:
-    """Enable or disable the split-K path of fp8_gemm_nt; returns the previous setting."""
-    return bool(lib.dg_set_split_k(int(bool(enable))))

@@ -19,7 +19,6 @@ constexpr int kMaxMaskedGroups = 1024;
 constexpr int kMaxDevices = 64;
 
 int g_num_cus_override = 0;
-int g_split_k_enabled = 1;
 int g_device_cus[kMaxDevices] = {0};
 
 // Compute units of the current device (ignores the override).
@@ -80,38 +79,15 @@ GemmInstance choose_dense(int64_t m, int64_t n, int cus) {
 }
 
 // ---- split-K for small M (too few output tiles to keep the CUs streaming B)
+//
+// Workspace layout (caller-owned): a fixed block of kSplitCounters int32
+// arrival counters (one per output tile; zero before first use, left zero by
+// every completed call), then the fp32 partial tiles [tiles][splits][BM*BN].
+// The counter block never moves, so one workspace serves problems of any shape.
 
-constexpr int64_t kSplitWsBytes = 64ll << 20;   // fp32 partial tiles
-constexpr int kSplitCounters = 1 << 16;         // arrival counters (one per output tile)
-
-struct SplitWorkspace {
-  float* ws = nullptr;
-  int* counters = nullptr;
-};
-SplitWorkspace g_split_ws[kMaxDevices];
-
-// Allocated on a device's first split-K call and kept for the process lifetime;
-// the counters start at zero and every kernel leaves them at zero.
-dg_status split_workspace(SplitWorkspace*& out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DG_ERROR_LAUNCH;
-  SplitWorkspace& w = g_split_ws[dev];
-  if (!w.ws) {
-    void* ws = nullptr;
-    void* cnt = nullptr;
-    if (hipMalloc(&ws, kSplitWsBytes) != hipSuccess) return DG_ERROR_LAUNCH;
-    if (hipMalloc(&cnt, kSplitCounters * sizeof(int)) != hipSuccess ||
-        hipMemset(cnt, 0, kSplitCounters * sizeof(int)) != hipSuccess) {
-      (void)hipFree(ws);
-      if (cnt) (void)hipFree(cnt);
-      return DG_ERROR_LAUNCH;
-    }
-    w.ws = static_cast<float*>(ws);
-    w.counters = static_cast<int*>(cnt);
-  }
-  out = &w;
-  return DG_SUCCESS;
-}
+constexpr int kSplitCounters = 1 << 16;
+constexpr int64_t kSplitCounterBytes = kSplitCounters * 4;     // 256 KiB
+constexpr int64_t kMaxSplitPartialBytes = 64ll << 20;           // plans larger than this are not considered
 
 struct DensePlan {
   GemmInstance inst;
@@ -175,7 +151,7 @@ DensePlan plan_dense(int64_t m, int64_t n, int64_t k, int cus, bool allow_split)
     const int64_t tiles = ceil_div(m, info.bm) * ceil_div(n, info.bn);
     const int64_t max_splits = allow_split && tiles <= kSplitCounters ? kblocks / kMinKbPerSplit : 1;
     for (int64_t s = 1; s <= max_splits || s == 1; ++s) {
-      if (s > 1 && tiles * s * info.bm * info.bn * (int64_t)sizeof(float) > kSplitWsBytes) break;
+      if (s > 1 && tiles * s * info.bm * info.bn * (int64_t)sizeof(float) > kMaxSplitPartialBytes) break;
       const DensePlan pl = make_plan(inst, m, n, kblocks, s);
       if (pl.splits != s && s > 1) continue;   // same as a smaller split count
       const double t = plan_seconds(pl, cus);
@@ -183,6 +159,13 @@ DensePlan plan_dense(int64_t m, int64_t n, int64_t k, int cus, bool allow_split)
     }
   }
   return best;
+}
+
+// Workspace bytes a plan needs (0 for an unsplit plan).
+int64_t plan_workspace_bytes(const DensePlan& pl) {
+  if (pl.splits <= 1) return 0;
+  const InstanceInfo info = instance_info(pl.inst);
+  return kSplitCounterBytes + pl.tiles * pl.splits * (int64_t)info.bm * info.bn * (int64_t)sizeof(float);
 }
 
 // Contiguous layout: the group of a tile is read per 128 rows, so BM = 128.
@@ -221,14 +204,21 @@ DG_EXPORT const char* dg_status_string(dg_status status) {
   return "DG_ERROR_UNKNOWN";
 }
 
-DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
-                                   const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
-                                   void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* stream) {
+DG_EXPORT size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  return (size_t)plan_workspace_bytes(plan_dense(m, n, k, hw_cus(), true));
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                      const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                      void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* ws,
+                                      size_t ws_bytes, void* stream) {
   if (m < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
   if (m == 0 || n == 0) return DG_SUCCESS;
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
   if (st != DG_SUCCESS) return st;
   if (!offsets_fit(m, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
+  if (ws && !aligned(ws, 16)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
   p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
@@ -237,19 +227,26 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   // The plan (and so the summation order) follows the hardware CU count, never
-  // the grid-width override, so results do not depend on the override.
-  const DensePlan plan = plan_dense(m, n, k, hw_cus(), g_split_k_enabled != 0);
+  // the grid-width override, so results do not depend on the override.  A
+  // split plan runs only when the caller's workspace holds it.
+  DensePlan plan = plan_dense(m, n, k, hw_cus(), ws != nullptr);
+  const int64_t need = plan_workspace_bytes(plan);
+  if (need > 0 && (int64_t)ws_bytes < need) plan = plan_dense(m, n, k, hw_cus(), false);
   if (plan.splits > 1) {
-    SplitWorkspace* w = nullptr;
-    const dg_status ws_st = split_workspace(w);
-    if (ws_st != DG_SUCCESS) return ws_st;
-    p.ws = w->ws;
-    p.counters = w->counters;
+    p.counters = static_cast<int*>(ws);
+    p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kSplitCounterBytes);
     p.splits = plan.splits;
     p.kb_per_split = plan.kb_per_split;
     return launch(plan.inst, kDenseSplitK, p, plan.tiles * plan.splits, static_cast<hipStream_t>(stream));
   }
   return launch(plan.inst, kDense, p, plan.tiles, static_cast<hipStream_t>(stream));
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                   const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                   void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* stream) {
+  return dg_fp8_gemm_nt_ws(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, m, n, k, nullptr, 0,
+                           stream);
 }
 
 DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
@@ -374,8 +371,3 @@ DG_EXPORT dg_status dg_set_num_cus(int num_cus) {
 
 DG_EXPORT int dg_get_num_cus(void) { return device_cus(); }
 
-DG_EXPORT int dg_set_split_k(int enable) {
-  const int prev = g_split_k_enabled;
-  g_split_k_enabled = enable ? 1 : 0;
-  return prev;
-}

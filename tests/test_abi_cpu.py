@@ -76,6 +76,29 @@ def test_dense_validation(lib):
     assert _gemm(lib, n=0) == 0
 
 
+def test_workspace_entry_validation_and_size(lib):
+    i = ctypes.c_int64
+    f = lib.dg_fp8_gemm_nt_ws
+    f.argtypes = [ctypes.c_void_p, i, ctypes.c_void_p, i, i, ctypes.c_void_p, i, ctypes.c_void_p, i, i,
+                  ctypes.c_void_p, i, i, i, i, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def call(ws, ws_bytes, **kw):
+        a = dict(lda=512, sfa_sm=4, sfa_sk=1, ldb=512, sfb_sn=4, sfb_sk=1, ldd=256, m=128, n=256, k=512, a=P)
+        a.update(kw)
+        return f(a["a"], a["lda"], P, a["sfa_sm"], a["sfa_sk"], P, a["ldb"], P, a["sfb_sn"], a["sfb_sk"], P,
+                 a["ldd"], a["m"], a["n"], a["k"], ws, ws_bytes, None)
+
+    assert call(ctypes.c_void_p(0x10008), 1 << 20) == 2     # workspace not 16-byte aligned
+    assert call(None, 0, a=None) == 1                        # validation as in dg_fp8_gemm_nt
+    assert call(P, 1 << 20, m=0) == 0                        # empty problem
+    size = lib.dg_fp8_gemm_nt_workspace_size
+    size.restype = ctypes.c_size_t
+    size.argtypes = [i, i, i]
+    assert size(4096, 4096, 7168) == 0                       # enough tiles: never split
+    assert size(64, 2112, 7168) > 256 * 1024                 # counter block + partial tiles
+    assert size(0, 2112, 7168) == 0 and size(64, 2112, 7000) == 0
+
+
 def test_contiguous_validation(lib):
     f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
     i = ctypes.c_int64

@@ -107,8 +107,8 @@ def test_deterministic_and_independent_of_grid_width(m, n, k):
 # Small M with deep K: the output has too few tiles for the device, so the K
 # blocks are split over several workgroups per output tile (partials summed in
 # split order by the last one to arrive).
-SPLIT = [(1, 8, 1024), (16, 1536, 2048), (64, 520, 4096), (65, 8, 640), (100, 264, 1024),
-         (128, 2112, 1536), (129, 264, 1536), (77, 136, 1280)]
+SPLIT = [(1, 8, 4096), (16, 1536, 2048), (64, 520, 4096), (77, 136, 1280), (128, 2112, 1536),
+         (129, 264, 1536), (8, 256, 8192), (200, 1032, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", SPLIT)
@@ -116,27 +116,39 @@ def test_split_k_parity_and_agreement(m, n, k):
     print(f"split-K {m}x{n}x{k}", flush=True)
     qa, sa, qb, sb = _host_problem(m, n, k, seed=m * 11 + n * 5 + k)
     want = ogemm.gemm_nt(qa, sa, qb, sb)
-    split = _gpu_dense(qa, sa, qb, sb)
+    need = dg.workspace_size(m, n, k)
+    assert need > 0, "shape expected to split"
+    ws = torch.zeros(need, dtype=torch.uint8, device=device())
+    a, b = (upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb))
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d, workspace=ws)
+    torch.cuda.synchronize()
+    split = bits(d)
     assert_gemm_close(split, want, f"split {m}x{n}x{k}")
-    # a second call reuses the workspace and its (reset) arrival counters
-    assert np.array_equal(split, _gpu_dense(qa, sa, qb, sb))
-    prev = dg.set_split_k(False)
-    try:
-        plain = _gpu_dense(qa, sa, qb, sb)
-    finally:
-        dg.set_split_k(prev)
-    assert_gemm_close(plain, want, f"unsplit {m}x{n}x{k}")
+    # the call left the counter block zero; a second call reuses the workspace
+    assert int(ws[:256 * 1024].count_nonzero()) == 0
+    d2 = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d2, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(split, bits(d2))
+    # no workspace (and a too-small one): the unsplit kernel
+    for w in (None, torch.zeros(need - 16, dtype=torch.uint8, device=device())):
+        d3 = sentinel_like((m, n))
+        dg.fp8_gemm_nt(a, b, d3, workspace=w)
+        torch.cuda.synchronize()
+        assert_gemm_close(bits(d3), want, f"unsplit {m}x{n}x{k}")
 
 
 def test_split_k_consecutive_problems_share_the_workspace():
-    """Back-to-back calls of different shapes on one stream, no host sync between."""
-    probs = [_host_problem(m, n, k, seed=40 + i)
-             for i, (m, n, k) in enumerate([(64, 1032, 2048), (120, 264, 4096), (8, 2048, 1024)])]
+    """Back-to-back calls of different shapes on one stream and one workspace, no host sync between."""
+    shapes = [(64, 1032, 2048), (120, 264, 4096), (8, 2048, 1024)]
+    probs = [_host_problem(m, n, k, seed=40 + i) for i, (m, n, k) in enumerate(shapes)]
+    ws = torch.zeros(max(dg.workspace_size(*s) for s in shapes), dtype=torch.uint8, device=device())
     outs = []
     for qa, sa, qb, sb in probs:
         m, n = qa.shape[0], qb.shape[0]
         d = sentinel_like((m, n))
-        dg.fp8_gemm_nt((upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb)), d)
+        dg.fp8_gemm_nt((upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb)), d, workspace=ws)
         outs.append(d)
     torch.cuda.synchronize()
     for (qa, sa, qb, sb), d in zip(probs, outs):

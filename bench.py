@@ -9,8 +9,8 @@ library's own cast kernels) and resident in HBM before timing.  ``value`` is
 whole-step TFLOPS (2*M*N*K summed over the step / wall time of K steps).
 
 The JSON line also carries:
-* ``roofline``: the dominant kernel (the 128x256-tile dense instance, which runs
-  the M=4096 shapes), algorithmic FLOPs per launch / its average launch time
+* ``roofline``: the dominant kernel (the tile/split instance that takes most of
+  the step), algorithmic FLOPs per launch / its average launch time
   measured with HIP events on the launch stream inside the timed steps, against
   the 5.0 PFLOP/s dense FP8 MFMA peak;
 * ``cpu_baseline``: the CPU oracle timed on the full 4096x4096x7168 GEMM (4 runs);
@@ -42,10 +42,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def mn_major(rows, kblocks, dev, groups=None):
+    """Scale buffer for A in the MN-major ("transposed") layout the GEMM reads
+    best: element (row, kb) at kb * rows + row."""
+    if groups is None:
+        return torch.empty((kblocks, rows), dtype=torch.float32, device=dev).t()
+    return torch.empty((groups, kblocks, rows), dtype=torch.float32, device=dev).transpose(1, 2)
+
+
 def make_dense(dg, m, n, k, seed, dev):
     a32 = synth.draw_activation_device(m, k, seed, dev)
     b32 = synth.draw_weight_device(n, k, seed, 0, dev)
-    qa, sa = dg.per_token_cast_fp8(a32)
+    qa, sa = dg.per_token_cast_fp8(a32, sf=mn_major(m, k // 128, dev))
     qb, sb = dg.per_block_cast_fp8(b32)
     del a32, b32
     d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -92,7 +100,7 @@ def bench_extras(dg, dev, reps):
         valid = torch.as_tensor(np.nonzero(m_indices >= 0)[0], device=dev)
         a32 = torch.zeros((m_total, k), dtype=torch.float32, device=dev)
         a32[valid] = synth.draw_activation_device(int(valid.numel()), k, seed, dev)
-        qa, sa = dg.per_token_cast_fp8(a32)
+        qa, sa = dg.per_token_cast_fp8(a32, sf=mn_major(m_total, k // 128, dev))
         del a32
         qb = torch.empty((8, n, k), dtype=torch.float8_e4m3fn, device=dev)
         sb = torch.empty((8, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
@@ -109,8 +117,11 @@ def bench_extras(dg, dev, reps):
 
         masked_m = synth.config3_masked_m(idx)
         seed = synth.seed_for(3, idx)
-        a32 = synth.draw_activation_device(16 * 256, k, seed, dev)
-        qa, sa = dg.per_token_cast_fp8(a32)
+        a32 = synth.draw_activation_device(16 * 256, k, seed, dev).view(16, 256, k)
+        qa = torch.empty((16, 256, k), dtype=torch.float8_e4m3fn, device=dev)
+        sa = mn_major(256, k // 128, dev, groups=16)
+        for g in range(16):
+            dg.per_token_cast_fp8(a32[g], q=qa[g], sf=sa[g])
         del a32
         qb = torch.empty((16, n, k), dtype=torch.float8_e4m3fn, device=dev)
         sb = torch.empty((16, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
@@ -118,8 +129,7 @@ def bench_extras(dg, dev, reps):
             dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), q=qb[g], sf=sb[g])
         d = torch.empty((16, 256, n), dtype=torch.bfloat16, device=dev)
         mm = torch.from_numpy(masked_m).to(dev)
-        qa3, sa3 = qa.view(16, 256, k), sa.view(16, 256, k // 128)
-        ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa3, sa3), (qb, sb), d, mm, 128), reps, flush)
+        ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm, 128), reps, flush)
         useful = 2.0 * int(masked_m.sum()) * n * k
         b_bytes = 16 * n * k
         out[f"masked_G16_{n}x{k}"] = {
@@ -134,7 +144,7 @@ def bench_extras(dg, dev, reps):
     valid = torch.as_tensor(np.nonzero(m_indices >= 0)[0], device=dev)
     a32 = torch.zeros((m_total, k), dtype=torch.float32, device=dev)
     a32[valid] = synth.draw_activation_device(int(valid.numel()), k, seed, dev)
-    qa, sa = dg.per_token_cast_fp8(a32, ue8m0=True)
+    qa, sa = dg.per_token_cast_fp8(a32, ue8m0=True, sf=mn_major(m_total, k // 128, dev))
     del a32
     qb = torch.empty((256, n, k), dtype=torch.float8_e4m3fn, device=dev)
     sb = torch.empty((256, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
@@ -216,7 +226,6 @@ def main():
         probs.append(make_dense(dg, m, n, k, synth.seed_for(1, idx), dev))
     torch.cuda.synchronize()
     flops = [2.0 * m * n * k for (m, n, k) in shapes]
-    big = [i for i, (m, _, _) in enumerate(shapes) if m == 4096] or list(range(len(shapes)))
 
     def step(events=None):
         for i, (a, b, d) in enumerate(probs):
@@ -243,8 +252,17 @@ def main():
     per_launch = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(shapes))]
                            for s in range(args.steps)])      # ms
     mean_ms = per_launch.mean(axis=0)
-    dom_time = float(mean_ms[big].mean())                    # average launch duration of the big-tile kernel
-    dom_flops = float(np.mean([flops[i] for i in big]))      # algorithmic FLOPs per launch (mean over its launches)
+    # The dominant kernel: the (tile, split) instance that takes most of the step.
+    # Its achieved rate = algorithmic FLOPs per launch / average launch duration,
+    # both averaged over that instance's launches in the timed steps.
+    cfgs = [dg.tile_config(m, n, k) for (m, n, k) in shapes]
+    by_cfg = {}
+    for i, c in enumerate(cfgs):
+        by_cfg.setdefault(c, []).append(i)
+    dom_cfg = max(by_cfg, key=lambda c: sum(mean_ms[i] for i in by_cfg[c]))
+    big = by_cfg[dom_cfg]
+    dom_time = float(mean_ms[big].mean())
+    dom_flops = float(np.mean([flops[i] for i in big]))
     achieved = dom_flops / (dom_time * 1e-3) / 1e12
     per_shape = []
     for i, (m, n, k) in enumerate(shapes):
@@ -277,7 +295,9 @@ def main():
                    "gemms_per_step": len(shapes), "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_kernel<Cfg<128,256,2,2,3>, dense> on the five M=4096 shapes",
+                     "kernel": "dense %dx%d-tile GEMM%s" % (dom_cfg[0], dom_cfg[1],
+                                                            "" if dom_cfg[2] == 1 else ", split-K %d" % dom_cfg[2]),
+                     "shapes": ["%dx%dx%d" % shapes[i] for i in big],
                      "avg_launch_us": round(dom_time * 1e3, 2), "flops_per_launch": dom_flops},
         "per_shape": per_shape,
     }

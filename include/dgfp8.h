@@ -113,6 +113,14 @@ dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda,
  * and the device's compute-unit count. */
 size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k);
 
+/* The output tile (block_m x block_n) and K split count dg_fp8_gemm_nt_ws
+ * would use for this problem with a workspace of ws_bytes (0: none).  For
+ * profiling and logs; the choice never changes results beyond the split-K
+ * note above.  Errors: null outputs or non-positive sizes ->
+ * DG_ERROR_INVALID_VALUE, k % 128 != 0 -> DG_ERROR_NOT_SUPPORTED. */
+dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, size_t ws_bytes,
+                                     int* block_m, int* block_n, int* splits);
+
 /*
  * M-grouped GEMM, contiguous layout (MoE prefill / training forward).
  * The rows of all groups are concatenated along M; each group's segment is

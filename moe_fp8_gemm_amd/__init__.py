@@ -48,6 +48,7 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt_ws": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
                            _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
     "dg_fp8_gemm_nt_workspace_size": ([_i64, _i64, _i64], ctypes.c_size_t),
+    "dg_fp8_gemm_nt_tile_config": ([_i64, _i64, _i64, ctypes.c_size_t, _p, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -105,6 +106,15 @@ _workspaces = {}
 def workspace_size(m: int, n: int, k: int) -> int:
     """Bytes of split-K workspace fp8_gemm_nt can use for this problem (0: never splits)."""
     return int(lib.dg_fp8_gemm_nt_workspace_size(int(m), int(n), int(k)))
+
+
+def tile_config(m: int, n: int, k: int, workspace: bool = True) -> Tuple[int, int, int]:
+    """(block_m, block_n, splits) fp8_gemm_nt uses for this problem (with the auto workspace, or none)."""
+    bm, bn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    ws = workspace_size(m, n, k) if workspace else 0
+    _check(lib.dg_fp8_gemm_nt_tile_config(int(m), int(n), int(k), ws, ctypes.byref(bm), ctypes.byref(bn),
+                                          ctypes.byref(sp)), "dg_fp8_gemm_nt_tile_config")
+    return bm.value, bn.value, sp.value
 
 
 def _auto_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
@@ -201,6 +211,10 @@ def _cast_out(rows: int, k: int, device, q: Optional[torch.Tensor], sf: Optional
         q = torch.empty((rows, k), dtype=torch.float8_e4m3fn, device=device)
     if sf is None:
         sf = torch.empty((sf_rows, k // 128), dtype=torch.float32, device=device)
+    if tuple(q.shape) != (rows, k) or q.dtype not in (torch.float8_e4m3fn, torch.uint8) or not q.is_cuda:
+        raise ValueError("q must be an E4M3 (or uint8) device tensor of shape (%d, %d)" % (rows, k))
+    if tuple(sf.shape) != (sf_rows, k // 128) or sf.dtype != torch.float32 or not sf.is_cuda:
+        raise ValueError("sf must be an fp32 device tensor of shape (%d, %d)" % (sf_rows, k // 128))
     return q, sf
 
 

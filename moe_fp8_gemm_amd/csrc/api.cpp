@@ -175,8 +175,8 @@ GemmInstance choose_contiguous(int64_t m_total, int64_t n, int cus) {
 }
 
 dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile_bound, hipStream_t stream) {
-  const int cus = device_cus();
-  int64_t grid = tile_bound < cus ? tile_bound : cus;
+  const int64_t slots = (int64_t)device_cus() * instance_info(inst).occ;
+  int64_t grid = tile_bound < slots ? tile_bound : slots;
   if (grid <= 0) return DG_SUCCESS;
   if (tile_bound > INT_MAX) return DG_ERROR_NOT_SUPPORTED;
   return launch_gemm(inst, v, p, (int)grid, stream) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
@@ -207,6 +207,20 @@ DG_EXPORT const char* dg_status_string(dg_status status) {
 DG_EXPORT size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
   return (size_t)plan_workspace_bytes(plan_dense(m, n, k, hw_cus(), true));
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, size_t ws_bytes, int* block_m,
+                                               int* block_n, int* splits) {
+  if (!block_m || !block_n || !splits) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
+  DensePlan plan = plan_dense(m, n, k, hw_cus(), ws_bytes > 0);
+  if ((int64_t)ws_bytes < plan_workspace_bytes(plan)) plan = plan_dense(m, n, k, hw_cus(), false);
+  const InstanceInfo info = instance_info(plan.inst);
+  *block_m = info.bm;
+  *block_n = info.bn;
+  *splits = plan.splits;
+  return DG_SUCCESS;
 }
 
 DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,

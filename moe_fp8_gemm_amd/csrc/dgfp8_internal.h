@@ -45,11 +45,13 @@ enum GemmInstance : int {
   kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
   kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves (small M, usually split over K)
   kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves (M <= 64, usually split over K)
+  kInstMidPair = 5,   // 128 x 128 output tiles, 8 waves, 2-stage pipeline, two workgroups per CU
   kNumInstances
 };
 
 struct InstanceInfo {
   int bm, bn;
+  int occ;   // workgroups resident per CU (persistent grid = CUs * occ)
 };
 InstanceInfo instance_info(GemmInstance inst);
 

@@ -90,12 +90,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int LAG_ = 2, int BBUF_ = 3>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BBUF_ = 3, int OCC_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int kStages = STAGES_;   // LDS stages; K blocks in flight = kStages - 1
-  static constexpr int kLag = LAG_;         // MFMAs between an MFMA and the FMAs promoting it
-  static constexpr int kBBuf = BBUF_;       // B fragments held in registers (streamed)
+  static constexpr int kBBuf = BBUF_;
+  static constexpr int kOcc = OCC_;         // workgroups resident per CU       // B fragments held in registers (streamed)
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -179,73 +179,103 @@ __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, 
   return (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// Scale application.  The product c = sa * sb of a row's A scale and the
+// wave's B scale is split as c = 2^e * m, m in [1, 4) carrying the signs.  The
+// block-scaled MFMA multiplies the K block's products by 2^e exactly: its E8M0
+// operands are the fp32 biased exponents of sb (B-row port, one per wave) and
+// of sa (A-row port, per lane: lane l supplies row l%16, the row its results
+// belong to).  The accumulator is kept in units of the current mantissa
+// product m = m_a * m_b: before a K block's MFMAs it is rescaled by
+// m_prev / m, and the epilogue multiplies by the last m.  The MFMA therefore
+// accumulates straight into acc, and no VALU instruction waits on an MFMA
+// result inside the K loop.  With power-of-two scales every mantissa is 1, so
+// the rescale is skipped (a wave-uniform test per K block).  Zero or
+// denormal scales have a biased exponent of 0, i.e. a weight of 2^-127 on
+// that block; infinities and NaNs give NaN.
+__device__ __forceinline__ int scale_exponent(float s) {
+  return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
+}
+__device__ __forceinline__ float scale_mantissa(float s) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x807FFFFFu) | 0x3F800000u);
+}
+
+// The MFMAs of one K block.  RS: the accumulator is rescaled first, each
+// MFMA's 4 multiplies issued right after the previous MFMA, so that they run
+// while it executes instead of holding the matrix core between K blocks.
+template <class C, int V, int SD, bool RS>
+__device__ __forceinline__ void mfma_sequence(f32x4 (&acc)[C::MS][C::NS], const i32x8 (&af)[C::MS],
+                                              i32x8 (&bf)[C::kBBuf], const int (&ea)[C::MS], int eb,
+                                              const float (&ratio)[C::MS], DG_LAS uint8_t* lb, uint32_t off0,
+                                              uint32_t off1, const TileSrc<C>& tsrc, int kbd, int wave, int lane) {
+  constexpr int kDmaGap = C::kMfmas / C::kLoadsPerStage > 0 ? C::kMfmas / C::kLoadsPerStage : 1;
+  constexpr int kBBuf = C::kBBuf;
+  if constexpr (RS) acc[0][0] *= ratio[0];
+#pragma unroll
+  for (int j = 0; j < C::kMfmas; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int t = j / C::MS, ms = j % C::MS;
+    // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
+    // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
+    acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[t % kBBuf], af[ms], acc[ms][t], 0, 0,
+                                                                  0, eb, 0, ea[ms]);
+    if constexpr (RS) {
+      if (j + 1 < C::kMfmas) {
+        const int t1 = (j + 1) / C::MS, ms1 = (j + 1) % C::MS;
+        acc[ms1][t1] *= ratio[ms1];
+      }
+    }
+    const int tn = t + kBBuf - 1;
+    if (ms == 0 && tn < C::NS) bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
+    if (j % kDmaGap == 0 && j / kDmaGap < C::kLoadsPerStage)
+      issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, j / kDmaGap);
+  }
+}
+
 // One K block from LDS stage S.  MFMA order: B fragment t outer, A fragment ms
 // inner; A fragments and row scales are read once, B fragments stream through
-// three register buffers (fragment t+2 is read while t is multiplied).  The
-// promotion of MFMA j (4 FMAs) is issued after MFMA j+2: by then the result is
-// ready, the FMAs fill the wait states the MFMA would otherwise need, and the
-// matrix core always has the next MFMA queued.  sched_barrier(0) between the
-// groups keeps the compiler's scheduler from undoing that order.
+// kBBuf register buffers (fragment t + kBBuf - 1 is read while t is used).
 // off0/off1: this lane's byte offsets of its two 16-byte slots inside a 16-row
-// fragment (the same for A and B fragments).
+// fragment (the same for A and B fragments).  mant: per-row mantissa product
+// the accumulator is expressed in (carried across K blocks).
 // The DMA of a later K block (kbd into stage SD) is spread over the MFMA
 // sequence, one instruction every kDmaGap MFMAs: issued back to back after the
 // barrier, the address unit would take them one by one and hold the waves at
-// issue, leaving the matrix cores idle.  No branches here: past the last K block
-// the caller passes the last block again (a harmless reload into a free stage).
+// issue, leaving the matrix cores idle.  No branches in the DMA: past the last
+// K block the caller passes the last block again (a harmless reload into a
+// free stage).  sched_barrier(0) between the groups keeps that spread.
 template <class C, int V, int S, int SD>
-__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], uint32_t off0, uint32_t off1, int wr,
-                                              int wc, int r16, const TileSrc<C>& tsrc, int kbd, int wave,
-                                              int lane) {
+__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], uint32_t off0,
+                                              uint32_t off1, int wr, int wc, int r16, const TileSrc<C>& tsrc,
+                                              int kbd, int wave, int lane) {
   constexpr int kDmaGap = C::kMfmas / C::kLoadsPerStage > 0 ? C::kMfmas / C::kLoadsPerStage : 1;
-  constexpr int kLag = C::kLag;
   constexpr int kBBuf = C::kBBuf;
   DG_LAS uint8_t* la = lds_a<C, V, S>() + wr * C::WM * kKBlock;
   DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
   DG_LAS float* ls = lds_s<C, V, S>();
   i32x8 af[C::MS];
-  float s[C::MS];
   i32x8 bf[kBBuf];
+  int ea[C::MS];
+  float ratio[C::MS];
   const float sb = ls[(C::kWaves - 1) * 64 + C::kSAPerWave + (wc * C::WN) / 128];
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) af[ms] = read_frag(la + ms * 16 * kKBlock, off0, off1);
 #pragma unroll
+  for (int t = 0; t < kBBuf - 1 && t < C::NS; ++t) bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
+  const int eb = scale_exponent(sb);
+  const float mb = scale_mantissa(sb);
+  bool rescale = false;
+#pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
     const int row = wr * C::WM + ms * 16 + r16;
-    s[ms] = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
+    const float sa = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
+    ea[ms] = scale_exponent(sa);
+    const float m = scale_mantissa(sa) * mb;
+    ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
+    rescale |= ratio[ms] != 1.0f;
+    mant[ms] = m;
   }
-#pragma unroll
-  for (int t = 0; t < kBBuf - 1 && t < C::NS; ++t) bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
-#pragma unroll
-  for (int ms = 0; ms < C::MS; ++ms) s[ms] *= sb;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 p[kLag + 1];
-  constexpr int kM = C::kMfmas;
-#pragma unroll
-  for (int j = 0; j < kM + kLag; ++j) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (j < kM) {
-      const int t = j / C::MS, ms = j % C::MS;
-      // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
-      // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
-      p[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[t % kBBuf], af[ms], zero,
-                                                                          0, 0, 0, 0, 0, 0);
-      const int tn = t + kBBuf - 1;
-      if (ms == 0 && tn < C::NS) bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
-      if (j % kDmaGap == 0 && j / kDmaGap < C::kLoadsPerStage)
-        issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, j / kDmaGap);
-    }
-    if (j >= kLag) {
-      const int i = j - kLag;
-      const int t = i / C::MS, ms = i % C::MS;
-      f32x4& a = acc[ms][t];
-      const f32x4 q = p[i % (kLag + 1)];
-      a[0] = __builtin_fmaf(q[0], s[ms], a[0]);
-      a[1] = __builtin_fmaf(q[1], s[ms], a[1]);
-      a[2] = __builtin_fmaf(q[2], s[ms], a[2]);
-      a[3] = __builtin_fmaf(q[3], s[ms], a[3]);
-    }
-  }
+  (void)rescale;
+  mfma_sequence<C, V, SD, true>(acc, af, bf, ea, eb, ratio, lb, off0, off1, tsrc, kbd, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (C::kMfmas / kDmaGap < C::kLoadsPerStage) {
 #pragma unroll
@@ -258,13 +288,14 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], uint32
 // landed; every wave is done reading the stage kb-1 used), then compute kb while
 // the DMA of kb + kStages - 1 is issued into that freed stage.
 template <class C, int V, int S>
-__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], int kb, int kblocks,
-                                     int wave, int lane, uint32_t off0, uint32_t off1, int wr, int wc, int r16) {
+__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], int kb,
+                                     int kblocks, int wave, int lane, uint32_t off0, uint32_t off1, int wr, int wc,
+                                     int r16) {
   // Every step issues one DMA group, so kStages - 2 younger groups may stay in flight.
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage>::value);
   lds_barrier();
   const int kbd = kb + C::kStages - 1;
-  compute_stage<C, V, S, (S + C::kStages - 1) % C::kStages>(acc, off0, off1, wr, wc, r16, t,
+  compute_stage<C, V, S, (S + C::kStages - 1) % C::kStages>(acc, mant, off0, off1, wr, wc, r16, t,
                                                              kbd < kblocks ? kbd : kblocks - 1, wave, lane);
 }
 
@@ -286,7 +317,7 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& mt,
 
 template <class C, int V>
 __global__ void __launch_bounds__(C::kThreads)
-__attribute__((amdgpu_waves_per_eu(C::kWaves / 4, C::kWaves / 4)))
+__attribute__((amdgpu_waves_per_eu(C::kWaves * C::kOcc / 4, C::kWaves * C::kOcc / 4)))
 gemm_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -435,10 +466,13 @@ gemm_kernel(GemmParams p) {
     }
 
     f32x4 acc[C::MS][C::NS];
+    float mant[C::MS];
 #pragma unroll
-    for (int i = 0; i < C::MS; ++i)
+    for (int i = 0; i < C::MS; ++i) {
+      mant[i] = 1.0f;
 #pragma unroll
       for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 
     // ---- prologue: every wave is done with the previous tile's LDS here
     __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
@@ -454,18 +488,22 @@ gemm_kernel(GemmParams p) {
     // kStages blocks, then the remaining kbs % kStages blocks
     int kb = 0;
 #define DG_STEP(I) \
-    if constexpr (I < C::kStages) step<C, V, I>(t, acc, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+    if constexpr (I < C::kStages) step<C, V, I>(t, acc, mant, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
     for (; kb + C::kStages <= kbs; kb += C::kStages) {
       DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
     }
 #undef DG_STEP
 #define DG_TAIL(I)                     \
     if constexpr (I < C::kStages - 1) \
-      if (kb + I < kbs) step<C, V, I>(t, acc, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+      if (kb + I < kbs) step<C, V, I>(t, acc, mant, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
     DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
 #undef DG_TAIL
 
-    // ---- epilogue: bf16 RNE, 16-byte stores of 8 consecutive columns
+    // ---- epilogue: back from mantissa units, bf16 RNE, 16-byte stores of 8 consecutive columns
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+      for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
     uint16_t* D = p.d + (V == kMasked ? (int64_t)g * p.d_gs : 0);
     const int er16 = tl & 15, eq = tl >> 4;
     if constexpr (V == kDenseSplitK) {
@@ -544,11 +582,12 @@ gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
 }
 
-using CfgHuge = Cfg<256, 256, 4, 2, 2, 1, 2>;
+using CfgHuge = Cfg<256, 256, 4, 2, 2, 2>;
 using CfgSkinny128 = Cfg<128, 64, 4, 2, 3>;
 using CfgSkinny64 = Cfg<64, 64, 4, 2, 3>;
 using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
+using CfgMidPair = Cfg<128, 128, 4, 2, 2, 2, 2>;   // two workgroups per CU
 
 // Variants compiled per configuration: bit v of Mask set = variant v available.
 template <class C, int Mask>
@@ -581,11 +620,12 @@ constexpr int kDenseAndSplit = (1 << kDense) | (1 << kDenseSplitK);
 
 InstanceInfo instance_info(GemmInstance inst) {
   switch (inst) {
-    case kInstHuge: return {CfgHuge::BM, CfgHuge::BN};
-    case kInstSkinny128: return {CfgSkinny128::BM, CfgSkinny128::BN};
-    case kInstSkinny64: return {CfgSkinny64::BM, CfgSkinny64::BN};
-    case kInstLarge: return {CfgLarge::BM, CfgLarge::BN};
-    case kInstMid: return {CfgMid::BM, CfgMid::BN};
+    case kInstHuge: return {CfgHuge::BM, CfgHuge::BN, CfgHuge::kOcc};
+    case kInstSkinny128: return {CfgSkinny128::BM, CfgSkinny128::BN, CfgSkinny128::kOcc};
+    case kInstSkinny64: return {CfgSkinny64::BM, CfgSkinny64::BN, CfgSkinny64::kOcc};
+    case kInstLarge: return {CfgLarge::BM, CfgLarge::BN, CfgLarge::kOcc};
+    case kInstMid: return {CfgMid::BM, CfgMid::BN, CfgMid::kOcc};
+    case kInstMidPair: return {CfgMidPair::BM, CfgMidPair::BN, CfgMidPair::kOcc};
     default: return {0, 0};
   }
 }
@@ -597,6 +637,7 @@ hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int gr
     case kInstSkinny64: return launch_cfg<CfgSkinny64, kDenseAndSplit>(v, p, grid, stream);
     case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);
     case kInstMid: return launch_cfg<CfgMid, kAll>(v, p, grid, stream);
+    case kInstMidPair: return launch_cfg<CfgMidPair, kAll>(v, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

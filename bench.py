@@ -196,6 +196,31 @@ def cpu_baseline():
                       f"{len(os.sched_getaffinity(0))}"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.txt")
+GEMM_SOURCE = os.path.join(ROOT, "moe_fp8_gemm_amd", "csrc", "gemm_fp8.hip")
+
+
+def measured_traffic(cfg, shapes):
+    """HBM bytes per launch of the dominant instance, from the committed PMC
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a 1 GiB copy), or None
+    when there is none for this instance and shape set or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    want_shapes = ",".join("%dx%dx%d" % s for s in shapes)
+    if (kv.get("kernel_source_sha256") != sha or kv.get("tile") != "%dx%dx%d" % cfg
+            or kv.get("shapes") != want_shapes):
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +228,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="profiling aid: after the timed steps, copy a 1 GiB buffer 3 times (a kernel of known "
+                         "traffic, to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--only", default=None,
                     help="profiling aid: time only this M,N,K of the workload (e.g. 4096,4096,7168)")
     args = ap.parse_args()
@@ -264,6 +292,13 @@ def main():
     dom_time = float(mean_ms[big].mean())
     dom_flops = float(np.mean([flops[i] for i in big]))
     achieved = dom_flops / (dom_time * 1e-3) / 1e12
+    if args.calib_copy:
+        src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     per_shape = []
     for i, (m, n, k) in enumerate(shapes):
         per_shape.append({"m": m, "n": n, "k": k, "us_in_step": float(mean_ms[i] * 1e3),
@@ -294,7 +329,8 @@ def main():
                                "A 1x128 and B 128x128 fp32 block scales, bf16 out",
                    "gemms_per_step": len(shapes), "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(dom_cfg, [shapes[i] for i in big]),
                      "kernel": "dense %dx%d-tile GEMM%s" % (dom_cfg[0], dom_cfg[1],
                                                             "" if dom_cfg[2] == 1 else ", split-K %d" % dom_cfg[2]),
                      "shapes": ["%dx%dx%d" % shapes[i] for i in big],

@@ -188,9 +188,8 @@ __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, 
 // product m = m_a * m_b: before a K block's MFMAs it is rescaled by
 // m_prev / m, and the epilogue multiplies by the last m.  The MFMA therefore
 // accumulates straight into acc, and no VALU instruction waits on an MFMA
-// result inside the K loop.  With power-of-two scales every mantissa is 1, so
-// the rescale is skipped (a wave-uniform test per K block).  Zero or
-// denormal scales have a biased exponent of 0, i.e. a weight of 2^-127 on
+// result inside the K loop (with power-of-two scales every ratio is 1).  Zero
+// or denormal scales have a biased exponent of 0, i.e. a weight of 2^-127 on
 // that block; infinities and NaNs give NaN.
 __device__ __forceinline__ int scale_exponent(float s) {
   return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
@@ -202,6 +201,8 @@ __device__ __forceinline__ float scale_mantissa(float s) {
 // The MFMAs of one K block.  RS: the accumulator is rescaled first, each
 // MFMA's 4 multiplies issued right after the previous MFMA, so that they run
 // while it executes instead of holding the matrix core between K blocks.
+// (A wave-uniform branch between the RS and plain sequences, to skip the
+// multiplies for power-of-two scales, makes the compiler spill: not used.)
 template <class C, int V, int SD, bool RS>
 __device__ __forceinline__ void mfma_sequence(f32x4 (&acc)[C::MS][C::NS], const i32x8 (&af)[C::MS],
                                               i32x8 (&bf)[C::kBBuf], const int (&ea)[C::MS], int eb,
@@ -263,7 +264,6 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], float 
   for (int t = 0; t < kBBuf - 1 && t < C::NS; ++t) bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
   const int eb = scale_exponent(sb);
   const float mb = scale_mantissa(sb);
-  bool rescale = false;
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
     const int row = wr * C::WM + ms * 16 + r16;
@@ -271,10 +271,8 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], float 
     ea[ms] = scale_exponent(sa);
     const float m = scale_mantissa(sa) * mb;
     ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
-    rescale |= ratio[ms] != 1.0f;
     mant[ms] = m;
   }
-  (void)rescale;
   mfma_sequence<C, V, SD, true>(acc, af, bf, ea, eb, ratio, lb, off0, off1, tsrc, kbd, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (C::kMfmas / kDmaGap < C::kLoadsPerStage) {

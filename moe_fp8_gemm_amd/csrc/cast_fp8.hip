@@ -35,69 +35,96 @@ __device__ __forceinline__ float block_scale(float amax, int ue8m0) {
   return s;
 }
 
-// E4M3 code of t, |t| <= 448, round to nearest even, no flush to zero.
-__device__ __forceinline__ uint32_t e4m3_rne(float t) {
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u) {
-    // below 2^-6 the spacing is 2^-9: scale exactly and round to an integer 0..8
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    // keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  return code | sign;
+// Correctly rounded fl32(|x| / s) from y = RN(1/s) (Markstein): q = RN(|x|*y)
+// is within one ulp of the quotient, the remainder |x| - q*s is exact in one
+// FMA, and RN(q + rem*y) is the correctly rounded quotient.  Three VALU ops
+// per element instead of a full division.  s is normal and positive and every
+// quotient that can reach a non-zero E4M3 code is a normal fp32 number, as the
+// method requires.  The clamped magnitude gets x's sign back (so -0 stays -0).
+struct BlockDivisor {
+  float s, y;
+};
+__device__ __forceinline__ BlockDivisor make_divisor(float s) {
+  return {s, 1.0f / s};   // correctly rounded fp32 division, once per block
+}
+__device__ __forceinline__ float scaled(float x, BlockDivisor d) {
+#pragma clang fp contract(off)
+  const float a = fabsf(x);
+  const float q = a * d.y;
+  const float rem = __builtin_fmaf(-q, d.s, a);
+  const float t = fminf(__builtin_fmaf(rem, d.y, q), kE4M3Max);
+  return __builtin_copysignf(t, x);
 }
 
-__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, float s) {
-  auto one = [s](float x) {
-    float t = x / s;                              // correctly rounded fp32 division
-    t = fminf(fmaxf(t, -kE4M3Max), kE4M3Max);
-    return e4m3_rne(t);
-  };
-  return one(x0) | (one(x1) << 8) | (one(x2) << 16) | (one(x3) << 24);
+// Four E4M3 codes, byte i from x_i.  The hardware conversion rounds to nearest
+// even with E4M3 subnormals; it equals a bit-level RNE encoder on every fp32
+// value of magnitude <= 448 (checked exhaustively on gfx950), so the codes are
+// the method's.
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, BlockDivisor d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x0, d), scaled(x1, d), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x2, d), scaled(x3, d), v, true);
+  return (uint32_t)v;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Per-token mapping: a wave owns whole rows (grid-stride over rows); its four
+// 16-lane groups walk the row's 128-element blocks with a stride of 4, so one
+// pass reads 4 adjacent blocks (1 KB of bf16) per wave, and kUnroll passes are
+// loaded before any is used to keep several 16-byte loads in flight per lane.
+// No division in the index math.
+constexpr int kUnroll = 4;
+
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* src_row, int col, float (&x)[8]) {
+  if constexpr (kF32) {
+    const float* src = (const float*)src_row + col;
+    const f32x4 v0 = *(const f32x4*)src;
+    const f32x4 v1 = *(const f32x4*)(src + 4);
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+  } else {
+    const u32x4 v = *(const u32x4*)((const uint16_t*)src_row + col);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+}
+
 template <bool kF32>
 __global__ void __launch_bounds__(256) per_token_cast_kernel(CastParams p) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t kbs = p.k / 128;
-  const int64_t nblocks = p.rows * kbs;
-  for (int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16; blk < nblocks;
-       blk += (int64_t)gridDim.x * 16) {
-    const int64_t row = blk / kbs;
-    const int64_t kb = blk - row * kbs;
-    const int64_t col = kb * 128 + lane16 * 8;
-    float x[8];
-    if constexpr (kF32) {
-      const float* src = (const float*)p.x + row * p.ldx + col;
-      const f32x4 v0 = *(const f32x4*)src;
-      const f32x4 v1 = *(const f32x4*)(src + 4);
-      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-    } else {
-      const uint16_t* src = (const uint16_t*)p.x + row * p.ldx + col;
-      const u32x4 v = *(const u32x4*)src;
-      x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-      x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  const int grp = (threadIdx.x >> 4) & 3;
+  const int kbs = (int)(p.k / 128);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < p.rows; row += nwaves) {
+    const void* xrow = kF32 ? (const void*)((const float*)p.x + row * p.ldx)
+                            : (const void*)((const uint16_t*)p.x + row * p.ldx);
+    uint8_t* qrow = p.q + row * p.ldq;
+    float* srow = p.sf + row * p.sf_s0;
+    for (int kb0 = grp; kb0 < kbs; kb0 += 4 * kUnroll) {
+      // every value below is uniform over the 16 lanes of a block
+      float x[kUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (kb0 + 4 * u < kbs) load8<kF32>(xrow, (kb0 + 4 * u) * 128 + lane16 * 8, x[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kb = kb0 + 4 * u;
+        if (kb >= kbs) break;
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[u][i]));
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+        const BlockDivisor d = make_divisor(block_scale(amax, p.ue8m0));
+        u32x2 out;
+        out.x = quant4(x[u][0], x[u][1], x[u][2], x[u][3], d);
+        out.y = quant4(x[u][4], x[u][5], x[u][6], x[u][7], d);
+        *(u32x2*)(qrow + kb * 128 + lane16 * 8) = out;
+        if (lane16 == 0) srow[kb * p.sf_s1] = d.s;
+      }
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const float s = block_scale(amax, p.ue8m0);
-    u32x2 out;
-    out.x = quant4(x[0], x[1], x[2], x[3], s);
-    out.y = quant4(x[4], x[5], x[6], x[7], s);
-    *(u32x2*)(p.q + row * p.ldq + col) = out;
-    if (lane16 == 0) p.sf[row * p.sf_s0 + kb * p.sf_s1] = s;
   }
 }
 
@@ -133,25 +160,24 @@ __global__ void __launch_bounds__(256) per_block_cast_kernel(CastParams p) {
   if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-  const float s = block_scale(amax, p.ue8m0);
+  const BlockDivisor d = make_divisor(block_scale(amax, p.ue8m0));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = nb * 128 + i * 16 + rsub;
     if (row < p.rows) {
       u32x2 out;
-      out.x = quant4(x[i][0], x[i][1], x[i][2], x[i][3], s);
-      out.y = quant4(x[i][4], x[i][5], x[i][6], x[i][7], s);
+      out.x = quant4(x[i][0], x[i][1], x[i][2], x[i][3], d);
+      out.y = quant4(x[i][4], x[i][5], x[i][6], x[i][7], d);
       *(u32x2*)(p.q + row * p.ldq + col) = out;
     }
   }
-  if (threadIdx.x == 0) p.sf[nb * p.sf_s0 + kb * p.sf_s1] = s;
+  if (threadIdx.x == 0) p.sf[nb * p.sf_s0 + kb * p.sf_s1] = d.s;
 }
 
 }  // namespace
 
 hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus, hipStream_t stream) {
-  const int64_t nblocks = p.rows * (p.k / 128);
-  int64_t grid = (nblocks + 15) / 16;
+  int64_t grid = (p.rows + 3) / 4;               // one row per wave
   const int64_t cap = (int64_t)num_cus * 16;    // grid-stride beyond 16 workgroups per CU
   if (grid > cap) grid = cap;
   if (input_fp32)

@@ -90,6 +90,47 @@ def test_per_block_cast(n, ue8m0):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+def _boundary_blocks(rng, rows, k):
+    """Blocks whose quotients x/s land on and next to E4M3 rounding boundaries
+    for many different scales: each row gets its own amax (so its own s); the
+    other elements are s * (a midpoint between E4M3 neighbours, or a code value)
+    nudged by -2..+2 fp32 ulps, rounded to fp32."""
+    from oracle import e4m3 as oe4m3
+    vals = np.array(sorted(set(abs(float(v)) for v in oe4m3.DECODE_TABLE if np.isfinite(v))), np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    targets = np.concatenate([mids, vals[1:]])
+    x = np.empty((rows, k), np.float32)
+    for r in range(rows):
+        amax = np.float32(np.exp2(rng.uniform(-20, 20)) * rng.uniform(1, 2))
+        s = np.float32(max(amax, np.float32(1e-4)) / np.float32(448.0))
+        t = rng.choice(targets, k)
+        base = (t * np.float64(s)).astype(np.float32)
+        nudge = rng.integers(-2, 3, k).astype(np.int32)
+        xi = (base.view(np.int32) + nudge).view(np.float32)
+        xi[rng.random(k) < 0.5] *= -1
+        xi[::128] = amax                       # the block amax (quotient 448)
+        x[r] = np.clip(xi, -amax, amax)
+    return x
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_per_token_rounding_boundaries_many_scales(ue8m0):
+    rng = np.random.default_rng(77)
+    x = _boundary_blocks(rng, 256, 2048)
+    _check_cast(torch.from_numpy(x).to(device()), x, ue8m0, f"fp32 boundaries ue8m0={ue8m0}")
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_per_block_rounding_boundaries(ue8m0):
+    rng = np.random.default_rng(78)
+    w = _boundary_blocks(rng, 256, 1024)
+    q, s = dg.per_block_cast_fp8(torch.from_numpy(w).to(device()), ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    oq, os_ = quant.per_block_cast(w, ue8m0)
+    assert np.array_equal(codes(q), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
 @pytest.mark.parametrize("ue8m0", [False, True])
 def test_per_token_full_size_activation_sampled(ue8m0):
     x = synth.config4_cast_input()                         # bf16 [32768, 7168]

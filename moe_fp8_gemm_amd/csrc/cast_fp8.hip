@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) per_block_cast_kernel(CastParams p) {
 
 hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus, hipStream_t stream) {
   int64_t grid = (p.rows + 3) / 4;               // one row per wave
-  const int64_t cap = (int64_t)num_cus * 16;    // grid-stride beyond 16 workgroups per CU
+  const int64_t cap = (int64_t)num_cus * 32;    // grid-stride beyond 32 workgroups per CU
   if (grid > cap) grid = cap;
   if (input_fp32)
     hipLaunchKernelGGL(per_token_cast_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p);

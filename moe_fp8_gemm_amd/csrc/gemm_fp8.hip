@@ -94,8 +94,8 @@ template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BBUF_ =
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int kStages = STAGES_;   // LDS stages; K blocks in flight = kStages - 1
-  static constexpr int kBBuf = BBUF_;
-  static constexpr int kOcc = OCC_;         // workgroups resident per CU       // B fragments held in registers (streamed)
+  static constexpr int kBBuf = BBUF_;       // B fragments held in registers (streamed)
+  static constexpr int kOcc = OCC_;         // workgroups resident per CU
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -198,103 +198,122 @@ __device__ __forceinline__ float scale_mantissa(float s) {
   return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x807FFFFFu) | 0x3F800000u);
 }
 
-// The MFMAs of one K block.  RS: the accumulator is rescaled first, each
-// MFMA's 4 multiplies issued right after the previous MFMA, so that they run
-// while it executes instead of holding the matrix core between K blocks.
-// (A wave-uniform branch between the RS and plain sequences, to skip the
-// multiplies for power-of-two scales, makes the compiler spill: not used.)
-template <class C, int V, int SD, bool RS>
-__device__ __forceinline__ void mfma_sequence(f32x4 (&acc)[C::MS][C::NS], const i32x8 (&af)[C::MS],
-                                              i32x8 (&bf)[C::kBBuf], const int (&ea)[C::MS], int eb,
-                                              const float (&ratio)[C::MS], DG_LAS uint8_t* lb, uint32_t off0,
-                                              uint32_t off1, const TileSrc<C>& tsrc, int kbd, int wave, int lane) {
-  constexpr int kDmaGap = C::kMfmas / C::kLoadsPerStage > 0 ? C::kMfmas / C::kLoadsPerStage : 1;
-  constexpr int kBBuf = C::kBBuf;
-  if constexpr (RS) acc[0][0] *= ratio[0];
-#pragma unroll
-  for (int j = 0; j < C::kMfmas; ++j) {
-    __builtin_amdgcn_sched_barrier(0);
-    const int t = j / C::MS, ms = j % C::MS;
-    // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
-    // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
-    acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[t % kBBuf], af[ms], acc[ms][t], 0, 0,
-                                                                  0, eb, 0, ea[ms]);
-    if constexpr (RS) {
-      if (j + 1 < C::kMfmas) {
-        const int t1 = (j + 1) / C::MS, ms1 = (j + 1) % C::MS;
-        acc[ms1][t1] *= ratio[ms1];
-      }
-    }
-    const int tn = t + kBBuf - 1;
-    if (ms == 0 && tn < C::NS) bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
-    if (j % kDmaGap == 0 && j / kDmaGap < C::kLoadsPerStage)
-      issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, j / kDmaGap);
-  }
+// acc *= s, component by component: a splat of s would let the optimizer
+// widen the scalar load of s into a vector load over its neighbours, which
+// pins the ratio array in scratch memory.
+__device__ __forceinline__ void rescale(f32x4& a, float s) {
+  a.x *= s;
+  a.y *= s;
+  a.z *= s;
+  a.w *= s;
 }
 
-// One K block from LDS stage S.  MFMA order: B fragment t outer, A fragment ms
-// inner; A fragments and row scales are read once, B fragments stream through
-// kBBuf register buffers (fragment t + kBBuf - 1 is read while t is used).
+// Register state of one K block: A fragments, streamed B fragments, scale
+// exponents and the accumulator rescale ratios.
+template <class C>
+struct BlockRegs {
+  i32x8 af[C::MS];
+  i32x8 bf[C::kBBuf];
+  int ea[C::MS];
+  int eb;
+  float ratio[C::MS];
+};
+
+// LDS reads and scale math of the K block in stage S: all A fragments, the
+// first kBBuf - 1 B fragments, the E8M0 exponents and the mantissa ratios.
 // off0/off1: this lane's byte offsets of its two 16-byte slots inside a 16-row
 // fragment (the same for A and B fragments).  mant: per-row mantissa product
 // the accumulator is expressed in (carried across K blocks).
-// The DMA of a later K block (kbd into stage SD) is spread over the MFMA
-// sequence, one instruction every kDmaGap MFMAs: issued back to back after the
-// barrier, the address unit would take them one by one and hold the waves at
-// issue, leaving the matrix cores idle.  No branches in the DMA: past the last
-// K block the caller passes the last block again (a harmless reload into a
-// free stage).  sched_barrier(0) between the groups keeps that spread.
-template <class C, int V, int S, int SD>
-__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], uint32_t off0,
-                                              uint32_t off1, int wr, int wc, int r16, const TileSrc<C>& tsrc,
-                                              int kbd, int wave, int lane) {
-  constexpr int kDmaGap = C::kMfmas / C::kLoadsPerStage > 0 ? C::kMfmas / C::kLoadsPerStage : 1;
-  constexpr int kBBuf = C::kBBuf;
+template <class C, int V, int S>
+__device__ __forceinline__ void load_block(BlockRegs<C>& r, float (&mant)[C::MS], uint32_t off0, uint32_t off1,
+                                           int wr, int wc, int r16) {
   DG_LAS uint8_t* la = lds_a<C, V, S>() + wr * C::WM * kKBlock;
   DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
   DG_LAS float* ls = lds_s<C, V, S>();
-  i32x8 af[C::MS];
-  i32x8 bf[kBBuf];
-  int ea[C::MS];
-  float ratio[C::MS];
   const float sb = ls[(C::kWaves - 1) * 64 + C::kSAPerWave + (wc * C::WN) / 128];
 #pragma unroll
-  for (int ms = 0; ms < C::MS; ++ms) af[ms] = read_frag(la + ms * 16 * kKBlock, off0, off1);
+  for (int ms = 0; ms < C::MS; ++ms) r.af[ms] = read_frag(la + ms * 16 * kKBlock, off0, off1);
 #pragma unroll
-  for (int t = 0; t < kBBuf - 1 && t < C::NS; ++t) bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
-  const int eb = scale_exponent(sb);
+  for (int t = 0; t < C::kBBuf - 1 && t < C::NS; ++t) r.bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
+  r.eb = scale_exponent(sb);
   const float mb = scale_mantissa(sb);
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
     const int row = wr * C::WM + ms * 16 + r16;
     const float sa = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
-    ea[ms] = scale_exponent(sa);
+    r.ea[ms] = scale_exponent(sa);
     const float m = scale_mantissa(sa) * mb;
-    ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
+    r.ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
     mant[ms] = m;
-  }
-  mfma_sequence<C, V, SD, true>(acc, af, bf, ea, eb, ratio, lb, off0, off1, tsrc, kbd, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (C::kMfmas / kDmaGap < C::kLoadsPerStage) {
-#pragma unroll
-    for (int d = C::kMfmas / kDmaGap; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, d);
   }
 }
 
-// One K block kb in LDS stage S = kb % kStages: wait for our DMA of kb (with 3
-// stages the group of kb+1 may stay in flight), barrier (every wave's DMA of kb
-// landed; every wave is done reading the stage kb-1 used), then compute kb while
-// the DMA of kb + kStages - 1 is issued into that freed stage.
-template <class C, int V, int S>
-__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], int kb,
-                                     int kblocks, int wave, int lane, uint32_t off0, uint32_t off1, int wr, int wc,
-                                     int r16) {
-  // Every step issues one DMA group, so kStages - 2 younger groups may stay in flight.
+// MFMAs j in [J0, J1) of the K block in stage S.  Order: B fragment t = j / MS
+// outer, A fragment ms = j % MS inner; B fragment t + kBBuf - 1 is read while
+// t is used.  Each accumulator is rescaled right before its MFMA, its 4
+// multiplies issued after the previous MFMA so that they run while it
+// executes.  With DMA, this wave's DMA instructions for a later K block (kbd
+// into stage SD) are spread over the range, one every kDmaGap MFMAs (issued
+// back to back they would hold the wave at the address unit), the rest after
+// it.  No branches in the DMA: past the last K block the caller passes the
+// last block again (a harmless reload into a free stage).  sched_barrier(0)
+// between the groups keeps this order.
+template <class C, int V, int S, int SD, int J0, int J1, bool DMA>
+__device__ __forceinline__ void mfma_range(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r, uint32_t off0,
+                                           uint32_t off1, int wc, const TileSrc<C>& tsrc, int kbd, int wave,
+                                           int lane) {
+  constexpr int kN = J1 - J0;
+  constexpr int kDmaGap = kN / C::kLoadsPerStage > 0 ? kN / C::kLoadsPerStage : 1;
+  constexpr int kBBuf = C::kBBuf;
+  DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
+  rescale(acc[J0 % C::MS][J0 / C::MS], r.ratio[J0 % C::MS]);
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int t = j / C::MS, ms = j % C::MS;
+    // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
+    // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
+    acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.bf[t % kBBuf], r.af[ms], acc[ms][t], 0, 0,
+                                                                  0, r.eb, 0, r.ea[ms]);
+    if (j + 1 < J1) {
+      const int t1 = (j + 1) / C::MS, ms1 = (j + 1) % C::MS;
+      rescale(acc[ms1][t1], r.ratio[ms1]);
+    }
+    const int tn = t + kBBuf - 1;
+    if (ms == 0 && tn < C::NS) r.bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
+    if constexpr (DMA) {
+      if ((j - J0) % kDmaGap == 0 && (j - J0) / kDmaGap < C::kLoadsPerStage)
+        issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, (j - J0) / kDmaGap);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (DMA && kN / kDmaGap < C::kLoadsPerStage) {
+#pragma unroll
+    for (int d = kN / kDmaGap; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, d);
+  }
+}
+
+// Every step issues one DMA group, so kStages - 2 younger groups may stay in
+// flight when a wave waits for its DMA of the block it is about to read.
+template <class C>
+__device__ __forceinline__ void wait_block_dma() {
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage>::value);
+}
+
+// One K block kb in LDS stage S = kb % kStages (all waves in step): wait for our
+// DMA of kb, barrier (every wave's DMA of kb landed; every wave is done reading
+// the stage kb-1 used), then compute kb while the DMA of kb + kStages - 1 is
+// issued into that freed stage.
+template <class C, int V, int S>
+__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS],
+                                     BlockRegs<C>& r, int kb, int kblocks, int wave, int lane, uint32_t off0,
+                                     uint32_t off1, int wr, int wc, int r16) {
+  wait_block_dma<C>();
   lds_barrier();
   const int kbd = kb + C::kStages - 1;
-  compute_stage<C, V, S, (S + C::kStages - 1) % C::kStages>(acc, mant, off0, off1, wr, wc, r16, t,
-                                                             kbd < kblocks ? kbd : kblocks - 1, wave, lane);
+  load_block<C, V, S>(r, mant, off0, off1, wr, wc, r16);
+  mfma_range<C, V, S, (S + C::kStages - 1) % C::kStages, 0, C::kMfmas, true>(
+      acc, r, off0, off1, wc, t, kbd < kblocks ? kbd : kblocks - 1, wave, lane);
 }
 
 __device__ __forceinline__ int remap_for_xcd(int b, int grid) {
@@ -484,16 +503,17 @@ gemm_kernel(GemmParams p) {
 
     // ---- main loop over K blocks, LDS stage = kb % kStages: whole periods of
     // kStages blocks, then the remaining kbs % kStages blocks
+    BlockRegs<C> r;
     int kb = 0;
 #define DG_STEP(I) \
-    if constexpr (I < C::kStages) step<C, V, I>(t, acc, mant, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+    if constexpr (I < C::kStages) step<C, V, I>(t, acc, mant, r, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
     for (; kb + C::kStages <= kbs; kb += C::kStages) {
       DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
     }
 #undef DG_STEP
 #define DG_TAIL(I)                     \
     if constexpr (I < C::kStages - 1) \
-      if (kb + I < kbs) step<C, V, I>(t, acc, mant, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
+      if (kb + I < kbs) step<C, V, I>(t, acc, mant, r, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
     DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
 #undef DG_TAIL
 

@@ -17,9 +17,10 @@
 //    away (4 FMAs per lane) and needs no second accumulator set.
 //  * Operands are swapped in the MFMA: B rows feed the A port, A rows the B
 //    port.  A lane's four result registers then belong to ONE row of D, so a
-//    lane needs one sa value per 16-row sub-tile, and its 4*NS columns are
-//    made contiguous by the order in which B rows are placed in LDS
-//    ("fragment order"), which turns the epilogue into 16-byte stores.
+//    lane needs one sa value per 16-row sub-tile.  The order in which B rows
+//    are placed in LDS ("fragment order") gives each lane 8 consecutive
+//    columns per fragment pair, and the 4 lanes of a row adjacent groups of
+//    8, so that every epilogue store writes 64 contiguous bytes per row.
 //  * Global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4) into three
 //    LDS stages: while K block kb is multiplied, the DMAs of kb+1 and kb+2 are
 //    in flight.  The DMAs are waited for explicitly (s_waitcnt vmcnt) and the
@@ -67,13 +68,21 @@ __device__ __forceinline__ int swz16(int row) { return (row & 7) ^ ((row >> 3) &
 __device__ __forceinline__ uint32_t lds_addr(const DG_LAS void* p) {
   return (uint32_t)(uintptr_t)p;
 }
+// Wave-uniform value the compiler may not prove uniform (it is carried across
+// tiles in a loop): read it from the first active lane into scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const float* vaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds), "v"(vaddr) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(vaddr) : "memory", "m0");
 }
 
 // Workgroup barrier that orders LDS accesses only (lgkmcnt), leaving DMA and
@@ -250,9 +259,9 @@ __device__ __forceinline__ void load_block(BlockRegs<C>& r, float (&mant)[C::MS]
 
 // MFMAs j in [J0, J1) of the K block in stage S.  Order: B fragment t = j / MS
 // outer, A fragment ms = j % MS inner; B fragment t + kBBuf - 1 is read while
-// t is used.  Each accumulator is rescaled right before its MFMA, its 4
-// multiplies issued after the previous MFMA so that they run while it
-// executes.  With DMA, this wave's DMA instructions for a later K block (kbd
+// t is used.  Each accumulator is rescaled two MFMAs before its own: its 4
+// multiplies are issued after MFMA j - 2, so that MFMA j does not wait out the
+// VALU-write -> MFMA-read hazard on its accumulator.  With DMA, this wave's DMA instructions for a later K block (kbd
 // into stage SD) are spread over the range, one every kDmaGap MFMAs (issued
 // back to back they would hold the wave at the address unit), the rest after
 // it.  No branches in the DMA: past the last K block the caller passes the
@@ -267,6 +276,7 @@ __device__ __forceinline__ void mfma_range(f32x4 (&acc)[C::MS][C::NS], BlockRegs
   constexpr int kBBuf = C::kBBuf;
   DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
   rescale(acc[J0 % C::MS][J0 / C::MS], r.ratio[J0 % C::MS]);
+  if constexpr (J0 + 1 < J1) rescale(acc[(J0 + 1) % C::MS][(J0 + 1) / C::MS], r.ratio[(J0 + 1) % C::MS]);
 #pragma unroll
   for (int j = J0; j < J1; ++j) {
     __builtin_amdgcn_sched_barrier(0);
@@ -275,9 +285,9 @@ __device__ __forceinline__ void mfma_range(f32x4 (&acc)[C::MS][C::NS], BlockRegs
     // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
     acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.bf[t % kBBuf], r.af[ms], acc[ms][t], 0, 0,
                                                                   0, r.eb, 0, r.ea[ms]);
-    if (j + 1 < J1) {
-      const int t1 = (j + 1) / C::MS, ms1 = (j + 1) % C::MS;
-      rescale(acc[ms1][t1], r.ratio[ms1]);
+    if (j + 2 < J1) {
+      const int t2 = (j + 2) / C::MS, ms2 = (j + 2) % C::MS;
+      rescale(acc[ms2][t2], r.ratio[ms2]);
     }
     const int tn = t + kBBuf - 1;
     if (ms == 0 && tn < C::NS) r.bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
@@ -388,200 +398,157 @@ gemm_kernel(GemmParams p) {
     num_tiles = tiles_m * tiles_n * (V == kDenseSplitK ? p.splits : 1);
   }
 
-  for (int tile = remap_for_xcd(blockIdx.x, gridDim.x); tile < num_tiles; tile += gridDim.x) {
-    // ---- decode the tile
-    int mt, nt, g = 0, split = 0;
-    int64_t m_limit = p.m;   // rows that may be written
-    if constexpr (V == kMasked) {
-      // group: largest g with prefix[g] * tiles_n <= tile
-      int lo = 0, hi = p.num_groups;          // invariant: prefix[lo]*tn <= tile < prefix[hi]*tn
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (masked_prefix[mid] * tiles_n <= tile) lo = mid; else hi = mid;
-      }
-      g = lo;
-      const int mtiles_g = masked_prefix[g + 1] - masked_prefix[g];
-      const int local = tile - masked_prefix[g] * tiles_n;
-      nt = local / mtiles_g;
-      mt = local % mtiles_g;
-      int mm = p.masked_m[g];
-      mm = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
-      m_limit = mm;
-    } else if constexpr (V == kDenseSplitK) {
-      // consecutive units are the splits of one output tile: they run together
-      split = tile % p.splits;
-      raster(tile / p.splits, tiles_m, tiles_n, mt, nt);
-    } else {
-      raster(tile, tiles_m, tiles_n, mt, nt);
-      if constexpr (V == kContiguous) {
-        g = p.m_indices[(int64_t)mt * C::BM];
-        if (g < 0) continue;                  // whole block is padding
-      }
-    }
-    const int64_t m0 = (int64_t)mt * C::BM;
-    const int64_t n0 = (int64_t)nt * C::BN;
-    const int64_t a_rows = p.m;   // rows of A present in memory (per group when masked)
-
-    // Per-lane index math of this tile is done on a copy of the lane id that the
-    // compiler cannot see through, so that it is recomputed per tile instead of
-    // being hoisted out of the tile loop and kept live (or spilled) for the
-    // whole kernel.
-    int tl = lane;
-    asm volatile("" : "+v"(tl));
-
-    // ---- DMA sources: uniform bases, per-lane 32-bit offsets (host checks they fit)
-    TileSrc<C> t;
-    t.a_base = p.a + (V == kMasked ? (int64_t)g * p.a_gs : 0);
-    t.b_base = p.b + (V != kDense ? (int64_t)g * p.b_gs : 0);
-#pragma unroll
-    for (int j = 0; j < C::kAChunksPerWave; ++j) {
-      const int prow = (wave * C::kAChunksPerWave + j) * 8 + (tl >> 3);
-      int64_t row = m0 + prow;
-      row = row < a_rows ? row : a_rows - 1;
-      t.a_off[j] = (uint32_t)(row * p.lda) + (((tl & 7) ^ swz16(prow)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < C::kBChunksPerWave; ++j) {
-      // LDS row prow of the B stage holds, in fragment order, column
-      // n0 + wcol*WN + 4*NS*(fi/4) + 4*ft + fi%4 (ft = fragment, fi = row in it).
-      const int prow = (wave * C::kBChunksPerWave + j) * 8 + (tl >> 3);
-      const int wcol = prow / C::WN;
-      const int pl = prow % C::WN;
-      const int ft = pl / 16, fi = pl % 16;
-      int64_t col = n0 + wcol * C::WN + 4 * C::NS * (fi / 4) + 4 * ft + (fi % 4);
-      col = col < p.n ? col : p.n - 1;
-      t.b_off[j] = (uint32_t)(col * p.ldb) + (((tl & 7) ^ swz16(prow)) << 4);
-    }
-    {
-      const float* SFA = p.sfa + (V == kMasked ? (int64_t)g * p.sfa_gs : 0);
-      const float* SFB = p.sfb + (V != kDense ? (int64_t)g * p.sfb_gs : 0);
-      // Every lane points at a valid scale (the DMA is unconditional; see
-      // kScaleFloats).  Lanes whose slot is not used repeat the address of the
-      // wave's first A row, so that the load touches no cache line beyond those
-      // holding the scales the tile needs.
-      const int j = tl - C::kSAPerWave;
-      if (wave == C::kWaves - 1 && j >= 0 && j < C::kNSB) {
-        int64_t nb = n0 / 128 + j;
-        nb = nb < n_sblocks ? nb : n_sblocks - 1;
-        t.s_src = SFB + nb * p.sfb_sn;
-        t.s_kstride = p.sfb_sk;
+  // Tile state: position, group, K blocks and DMA sources.  okmask bit ms:
+  // this lane's row of sub-tile ms is written.  The epilogue's global loads
+  // (m_indices, masked_m) are done and consumed here, before the next tile's
+  // DMAs are issued: the compiler does not know of those DMAs, and a wait for
+  // a load placed after them would wait for them too.
+  struct Tile {
+    int mt, nt, g, split, kbs;
+    uint32_t okmask;
+    TileSrc<C> src;
+  };
+  auto decode = [&](int tile, Tile& s) -> bool {
+      int mt, nt, g = 0, split = 0;
+      int64_t m_limit = p.m;   // rows that may be written
+      if constexpr (V == kMasked) {
+        // group: largest g with prefix[g] * tiles_n <= tile
+        int lo = 0, hi = p.num_groups;          // invariant: prefix[lo]*tn <= tile < prefix[hi]*tn
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (masked_prefix[mid] * tiles_n <= tile) lo = mid; else hi = mid;
+        }
+        g = lo;
+        const int mtiles_g = masked_prefix[g + 1] - masked_prefix[g];
+        const int local = tile - masked_prefix[g] * tiles_n;
+        nt = local / mtiles_g;
+        mt = local % mtiles_g;
+        int mm = p.masked_m[g];
+        mm = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
+        m_limit = mm;
+      } else if constexpr (V == kDenseSplitK) {
+        // consecutive units are the splits of one output tile: they run together
+        split = tile % p.splits;
+        raster(tile / p.splits, tiles_m, tiles_n, mt, nt);
       } else {
-        int64_t row = m0 + wave * C::kSAPerWave + (tl < C::kSAPerWave ? tl : 0);
+        raster(tile, tiles_m, tiles_n, mt, nt);
+        if constexpr (V == kContiguous) {
+          g = p.m_indices[(int64_t)mt * C::BM];
+          if (g < 0) return false;              // whole block is padding
+        }
+      }
+      const int64_t m0 = (int64_t)mt * C::BM;
+      const int64_t n0 = (int64_t)nt * C::BN;
+      const int64_t a_rows = p.m;   // rows of A present in memory (per group when masked)
+
+      // Per-lane index math of this tile is done on a copy of the lane id that the
+      // compiler cannot see through, so that it is recomputed per tile instead of
+      // being hoisted out of the tile loop and kept live (or spilled) for the
+      // whole kernel.
+      int tl = lane;
+      asm volatile("" : "+v"(tl));
+
+      // ---- DMA sources: uniform bases, per-lane 32-bit offsets (host checks they fit)
+      TileSrc<C>& t = s.src;
+      t.a_base = p.a + (V == kMasked ? (int64_t)g * p.a_gs : 0);
+      t.b_base = p.b + (V != kDense ? (int64_t)g * p.b_gs : 0);
+#pragma unroll
+      for (int j = 0; j < C::kAChunksPerWave; ++j) {
+        const int prow = (wave * C::kAChunksPerWave + j) * 8 + (tl >> 3);
+        int64_t row = m0 + prow;
         row = row < a_rows ? row : a_rows - 1;
-        t.s_src = SFA + row * p.sfa_sm;
-        t.s_kstride = p.sfa_sk;
+        t.a_off[j] = (uint32_t)(row * p.lda) + (((tl & 7) ^ swz16(prow)) << 4);
       }
-    }
-
-    int kbs = kblocks;   // K blocks of this unit
-    if constexpr (V == kDenseSplitK) {
-      const int kb0 = split * p.kb_per_split;
-      kbs = min(p.kb_per_split, kblocks - kb0);
-      t.a_base += (int64_t)kb0 * kKBlock;
-      t.b_base += (int64_t)kb0 * kKBlock;
-      t.s_src += (int64_t)kb0 * t.s_kstride;
-    }
-
-    f32x4 acc[C::MS][C::NS];
-    float mant[C::MS];
 #pragma unroll
-    for (int i = 0; i < C::MS; ++i) {
-      mant[i] = 1.0f;
-#pragma unroll
-      for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- prologue: every wave is done with the previous tile's LDS here
-    __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
-    lds_barrier();
-    // K blocks 0 .. kStages-2 into stages 0 .. kStages-2 (the last block again
-    // where the unit has fewer)
-#define DG_PROLOGUE(I) \
-    if constexpr (I < C::kStages - 1) issue_dma<C, V, I>(t, I < kbs ? I : kbs - 1, wave, lane);
-    DG_PROLOGUE(0) DG_PROLOGUE(1) DG_PROLOGUE(2) DG_PROLOGUE(3) DG_PROLOGUE(4) DG_PROLOGUE(5) DG_PROLOGUE(6)
-#undef DG_PROLOGUE
-
-    // ---- main loop over K blocks, LDS stage = kb % kStages: whole periods of
-    // kStages blocks, then the remaining kbs % kStages blocks
-    BlockRegs<C> r;
-    int kb = 0;
-#define DG_STEP(I) \
-    if constexpr (I < C::kStages) step<C, V, I>(t, acc, mant, r, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
-    for (; kb + C::kStages <= kbs; kb += C::kStages) {
-      DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
-    }
-#undef DG_STEP
-#define DG_TAIL(I)                     \
-    if constexpr (I < C::kStages - 1) \
-      if (kb + I < kbs) step<C, V, I>(t, acc, mant, r, kb + I, kbs, wave, lane, off0, off1, wr, wc, r16);
-    DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
-#undef DG_TAIL
-
-    // ---- epilogue: back from mantissa units, bf16 RNE, 16-byte stores of 8 consecutive columns
-#pragma unroll
-    for (int ms = 0; ms < C::MS; ++ms)
-#pragma unroll
-      for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
-    uint16_t* D = p.d + (V == kMasked ? (int64_t)g * p.d_gs : 0);
-    const int er16 = tl & 15, eq = tl >> 4;
-    if constexpr (V == kDenseSplitK) {
-      // Publish this unit's partial tile, count arrivals; the last unit of the
-      // output tile adds all partials in split order (deterministic whatever the
-      // arrival order) and writes D.  Partials are kept in register order, not
-      // as a matrix: element c of acc[ms][j] of lane l of wave w sits at
-      // ((w * MS * NS + ms * NS + j) * 4 + c) * 64 + l, so that every store and
-      // load instruction covers 256 contiguous bytes.  The units of one tile may
-      // run on different XCDs, whose L2 caches are not coherent with each other
-      // for plain accesses: the partials move by device-scope relaxed atomic
-      // stores and loads (written through to / read from the device-coherent
-      // level), which avoids the L2-wide writeback and invalidate that a
-      // device-scope fence costs.
-      const int tile_mn = mt * tiles_n + nt;
-      float* part = p.ws + (int64_t)tile_mn * p.splits * (C::BM * C::BN) + wave * (C::kMfmas * 256) + tl;
-#pragma unroll
-      for (int ms = 0; ms < C::MS; ++ms)
-#pragma unroll
-        for (int j = 0; j < C::NS; ++j)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            __hip_atomic_store(part + (int64_t)split * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
-                               acc[ms][j][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // every partial store has been acknowledged before the arrival is counted
-      __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
-      __shared__ int last_flag;
-      __syncthreads();
-      if (threadIdx.x == 0)
-        last_flag = __hip_atomic_fetch_add(p.counters + tile_mn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    p.splits - 1;
-      __syncthreads();
-      if (!last_flag) continue;
-#pragma unroll
-      for (int ms = 0; ms < C::MS; ++ms)
-#pragma unroll
-        for (int j = 0; j < C::NS; ++j) acc[ms][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < p.splits; ++sp) {
-#pragma unroll
-        for (int ms = 0; ms < C::MS; ++ms)
-#pragma unroll
-          for (int j = 0; j < C::NS; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              acc[ms][j][c] += __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < C::kBChunksPerWave; ++j) {
+        // LDS row prow of the B stage holds, in fragment order, column
+        // n0 + wcol*WN + 32*(ft/2) + 8*(fi/4) + 4*(ft%2) + fi%4 (ft = fragment,
+        // fi = row in it).  Result lane group q = fi/4 then holds, from the
+        // fragment pair (2j, 2j+1), the 8 columns 32j + 8q .. 32j + 8q + 7: one
+        // store instruction writes 64 contiguous bytes of each of 16 rows.
+        const int prow = (wave * C::kBChunksPerWave + j) * 8 + (tl >> 3);
+        const int wcol = prow / C::WN;
+        const int pl = prow % C::WN;
+        const int ft = pl / 16, fi = pl % 16;
+        int64_t col = n0 + wcol * C::WN + 32 * (ft / 2) + 8 * (fi / 4) + 4 * (ft % 2) + (fi % 4);
+        col = col < p.n ? col : p.n - 1;
+        t.b_off[j] = (uint32_t)(col * p.ldb) + (((tl & 7) ^ swz16(prow)) << 4);
       }
-      // ready for the next call
-      if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+      {
+        const float* SFA = p.sfa + (V == kMasked ? (int64_t)g * p.sfa_gs : 0);
+        const float* SFB = p.sfb + (V != kDense ? (int64_t)g * p.sfb_gs : 0);
+        // Every lane points at a valid scale (the DMA is unconditional; see
+        // kScaleFloats).  Lanes whose slot is not used repeat the address of the
+        // wave's first A row, so that the load touches no cache line beyond those
+        // holding the scales the tile needs.
+        const int j = tl - C::kSAPerWave;
+        if (wave == C::kWaves - 1 && j >= 0 && j < C::kNSB) {
+          int64_t nb = n0 / 128 + j;
+          nb = nb < n_sblocks ? nb : n_sblocks - 1;
+          t.s_src = SFB + nb * p.sfb_sn;
+          t.s_kstride = p.sfb_sk;
+        } else {
+          int64_t row = m0 + wave * C::kSAPerWave + (tl < C::kSAPerWave ? tl : 0);
+          row = row < a_rows ? row : a_rows - 1;
+          t.s_src = SFA + row * p.sfa_sm;
+          t.s_kstride = p.sfa_sk;
+        }
+      }
+
+      int kbs = kblocks;   // K blocks of this unit
+      if constexpr (V == kDenseSplitK) {
+        const int kb0 = split * p.kb_per_split;
+        kbs = min(p.kb_per_split, kblocks - kb0);
+        t.a_base += (int64_t)kb0 * kKBlock;
+        t.b_base += (int64_t)kb0 * kKBlock;
+        t.s_src += (int64_t)kb0 * t.s_kstride;
+      }
+    // All of these are wave-uniform; say so, so that they stay in scalar
+    // registers across the tile loop.
+    t.a_base = uniform_ptr(t.a_base);
+    t.b_base = uniform_ptr(t.b_base);
+    s.mt = __builtin_amdgcn_readfirstlane(mt);
+    s.nt = __builtin_amdgcn_readfirstlane(nt);
+    s.g = __builtin_amdgcn_readfirstlane(g);
+    s.split = __builtin_amdgcn_readfirstlane(split);
+    s.kbs = __builtin_amdgcn_readfirstlane(kbs);
+    uint32_t okm = 0;
 #pragma unroll
     for (int ms = 0; ms < C::MS; ++ms) {
-      const int64_t row = m0 + wr * C::WM + ms * 16 + er16;
+      const int64_t row = m0 + wr * C::WM + ms * 16 + (tl & 15);
       bool ok = row < m_limit;
       if constexpr (V == kContiguous) ok = ok && (p.m_indices[row] >= 0);
-      if (!ok) continue;
-      uint16_t* drow = D + row * p.ldd;
+      okm |= (ok ? 1u : 0u) << ms;
+    }
+    s.okmask = okm;
+    return true;
+  };
+  // First tile at or after `tile` (stride gridDim.x) that is not skipped.
+  auto next_tile = [&](int tile, Tile& s) -> int {
+    for (; tile < num_tiles; tile += gridDim.x)
+      if (decode(tile, s)) break;
+    return tile;
+  };
+  // K blocks 0 .. kStages-2 into stages 0 .. kStages-2 (the last block again
+  // where the unit has fewer).
+  auto prologue = [&](const Tile& s) {
+#define DG_PROLOGUE(I) \
+    if constexpr (I < C::kStages - 1) issue_dma<C, V, I>(s.src, I < s.kbs ? I : s.kbs - 1, wave, lane);
+    DG_PROLOGUE(0) DG_PROLOGUE(1) DG_PROLOGUE(2) DG_PROLOGUE(3) DG_PROLOGUE(4) DG_PROLOGUE(5) DG_PROLOGUE(6)
+#undef DG_PROLOGUE
+  };
+  // bf16 RNE, 16-byte stores of 8 consecutive columns.
+  auto store_tile = [&](const Tile& s, f32x4 (&acc)[C::MS][C::NS]) {
+    uint16_t* D = p.d + (V == kMasked ? (int64_t)s.g * p.d_gs : 0);
+    const int er16 = lane & 15, eq = lane >> 4;
+    const int64_t m0 = (int64_t)s.mt * C::BM, n0 = (int64_t)s.nt * C::BN;
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms) {
+      if (!((s.okmask >> ms) & 1u)) continue;
+      uint16_t* drow = D + (m0 + wr * C::WM + ms * 16 + er16) * p.ldd;
 #pragma unroll
       for (int j = 0; j < C::NS / 2; ++j) {
-        const int64_t col = n0 + wc * C::WN + 4 * C::NS * eq + 8 * j;
+        const int64_t col = n0 + wc * C::WN + 32 * j + 8 * eq;
         if (col < p.n) {
           const f32x4 x0 = acc[ms][2 * j];
           const f32x4 x1 = acc[ms][2 * j + 1];
@@ -594,6 +561,108 @@ gemm_kernel(GemmParams p) {
         }
       }
     }
+  };
+  Tile cur;
+  int tile = next_tile(remap_for_xcd(blockIdx.x, gridDim.x), cur);
+  if (tile < num_tiles) prologue(cur);
+  while (tile < num_tiles) {
+    f32x4 acc[C::MS][C::NS];
+    float mant[C::MS];
+#pragma unroll
+    for (int i = 0; i < C::MS; ++i) {
+      mant[i] = 1.0f;
+#pragma unroll
+      for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- main loop over K blocks, LDS stage = kb % kStages: whole periods of
+    // kStages blocks, then the remaining kbs % kStages blocks
+    BlockRegs<C> r;
+    int kb = 0;
+#define DG_STEP(I) \
+    if constexpr (I < C::kStages) step<C, V, I>(cur.src, acc, mant, r, kb + I, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
+    for (; kb + C::kStages <= cur.kbs; kb += C::kStages) {
+      DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
+    }
+#undef DG_STEP
+#define DG_TAIL(I)                     \
+    if constexpr (I < C::kStages - 1) \
+      if (kb + I < cur.kbs) step<C, V, I>(cur.src, acc, mant, r, kb + I, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
+    DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
+#undef DG_TAIL
+
+    // ---- epilogue: back from mantissa units
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+      for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
+    Tile nxt;
+    const int ntile = next_tile(tile + gridDim.x, nxt);
+    if constexpr (V == kDenseSplitK) {
+      // Publish this unit's partial tile, count arrivals; the last unit of the
+      // output tile adds all partials in split order (deterministic whatever the
+      // arrival order) and writes D.  Partials are kept in register order, not
+      // as a matrix: element c of acc[ms][j] of lane l of wave w sits at
+      // ((w * MS * NS + ms * NS + j) * 4 + c) * 64 + l, so that every store and
+      // load instruction covers 256 contiguous bytes.  The units of one tile may
+      // run on different XCDs, whose L2 caches are not coherent with each other
+      // for plain accesses: the partials move by device-scope relaxed atomic
+      // stores and loads (written through to / read from the device-coherent
+      // level), which avoids the L2-wide writeback and invalidate that a
+      // device-scope fence costs.
+      const int tile_mn = cur.mt * tiles_n + cur.nt;
+      float* part = p.ws + (int64_t)tile_mn * p.splits * (C::BM * C::BN) + wave * (C::kMfmas * 256) + lane;
+#pragma unroll
+      for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+        for (int j = 0; j < C::NS; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            __hip_atomic_store(part + (int64_t)cur.split * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
+                               acc[ms][j][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every partial store has been acknowledged before the arrival is counted
+      __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
+      __shared__ int last_flag;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        last_flag = __hip_atomic_fetch_add(p.counters + tile_mn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    p.splits - 1;
+      __syncthreads();
+      if (last_flag) {
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+          for (int j = 0; j < C::NS; ++j) acc[ms][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < p.splits; ++sp) {
+#pragma unroll
+          for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+            for (int j = 0; j < C::NS; ++j)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                acc[ms][j][c] += __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // ready for the next call
+        if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_tile(cur, acc);
+      }
+      // every wave is done with this unit's LDS stages and its DMAs have landed
+      __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
+      lds_barrier();
+      if (ntile < num_tiles) prologue(nxt);
+    } else {
+      // Every wave is done reading this tile's LDS stages, and the DMAs its
+      // last steps re-issued into them have landed (only those are
+      // outstanding here): issue the next tile's first DMAs, then convert and
+      // store this tile while they are in flight.
+      __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
+      lds_barrier();
+      if (ntile < num_tiles) prologue(nxt);
+      store_tile(cur, acc);
+    }
+    cur = nxt;
+    tile = ntile;
   }
   // Tail steps re-issue the last K block's DMA into free stages: let them land
   // before this workgroup's LDS can be handed to another one.

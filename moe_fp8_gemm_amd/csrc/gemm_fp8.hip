@@ -30,6 +30,8 @@
 //    so that the 32 workgroups of one XCD work on neighbouring tiles (L2 per XCD).
 #include "dgfp8_internal.h"
 
+#include <utility>
+
 namespace dgfp8 {
 namespace {
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BBUF_ = 3, int OCC_ = 1>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BBUF_ = 2, int OCC_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int kStages = STAGES_;   // LDS stages; K blocks in flight = kStages - 1
@@ -129,23 +131,22 @@ struct Cfg {
   static_assert((kStages - 2) * kLoadsPerStage <= 63, "vmcnt range of the stage wait");
 };
 
-// LDS buffers, one variable per (config, variant, stage, kind): every kernel owns
-// its buffers, and distinct variables let the compiler's LDS-DMA wait tracking
-// tell the stages apart (otherwise each LDS read would wait for every DMA).
-template <class C, int V, int S>
-__device__ __forceinline__ DG_LAS uint8_t* lds_a() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[C::BM * kKBlock];
-  return (DG_LAS uint8_t*)buf;
+// LDS buffers, one array of kStages stages per (config, variant, kind): every
+// kernel owns its buffers.  The stage index is a run-time value.
+template <class C, int V>
+__device__ __forceinline__ DG_LAS uint8_t* lds_a(int stage) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[C::kStages * C::BM * kKBlock];
+  return (DG_LAS uint8_t*)buf + stage * (C::BM * kKBlock);
 }
-template <class C, int V, int S>
-__device__ __forceinline__ DG_LAS uint8_t* lds_b() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[C::BN * kKBlock];
-  return (DG_LAS uint8_t*)buf;
+template <class C, int V>
+__device__ __forceinline__ DG_LAS uint8_t* lds_b(int stage) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[C::kStages * C::BN * kKBlock];
+  return (DG_LAS uint8_t*)buf + stage * (C::BN * kKBlock);
 }
-template <class C, int V, int S>
-__device__ __forceinline__ DG_LAS float* lds_s() {
-  __shared__ __attribute__((aligned(16))) float buf[C::kScaleFloats];
-  return (DG_LAS float*)buf;
+template <class C, int V>
+__device__ __forceinline__ DG_LAS float* lds_s(int stage) {
+  __shared__ __attribute__((aligned(16))) float buf[C::kStages * C::kScaleFloats];
+  return (DG_LAS float*)buf + stage * C::kScaleFloats;
 }
 
 // DMA sources of one tile.  Bases are wave-uniform (scalar registers); per-lane
@@ -161,25 +162,25 @@ struct TileSrc {
 };
 
 // DMA instruction d (0 <= d < kLoadsPerStage) of this wave's share of K block kb
-// into LDS stage S: A chunks first, then B chunks, then the scales.
-template <class C, int V, int S>
-__device__ __forceinline__ void issue_dma_part(const TileSrc<C>& t, int kb, int wave, int lane, int d) {
+// into LDS stage st: A chunks first, then B chunks, then the scales.
+template <class C, int V>
+__device__ __forceinline__ void issue_dma_part(const TileSrc<C>& t, int kb, int st, int wave, int lane, int d) {
   constexpr int NA = C::kAChunksPerWave, NB = C::kBChunksPerWave;
   (void)lane;
   if (d < NA) {
-    dma16(t.a_base + (int64_t)kb * kKBlock, t.a_off[d], lds_addr(lds_a<C, V, S>()) + (wave * NA + d) * 1024);
+    dma16(t.a_base + (int64_t)kb * kKBlock, t.a_off[d], lds_addr(lds_a<C, V>(st)) + (wave * NA + d) * 1024);
   } else if (d < NA + NB) {
     const int j = d - NA;
-    dma16(t.b_base + (int64_t)kb * kKBlock, t.b_off[j], lds_addr(lds_b<C, V, S>()) + (wave * NB + j) * 1024);
+    dma16(t.b_base + (int64_t)kb * kKBlock, t.b_off[j], lds_addr(lds_b<C, V>(st)) + (wave * NB + j) * 1024);
   } else {
-    dma4(t.s_src + kb * t.s_kstride, lds_addr(lds_s<C, V, S>()) + wave * 64 * 4);
+    dma4(t.s_src + kb * t.s_kstride, lds_addr(lds_s<C, V>(st)) + wave * 64 * 4);
   }
 }
 
-template <class C, int V, int S>
-__device__ __forceinline__ void issue_dma(const TileSrc<C>& t, int kb, int wave, int lane) {
+template <class C, int V>
+__device__ __forceinline__ void issue_dma(const TileSrc<C>& t, int kb, int st, int wave, int lane) {
 #pragma unroll
-  for (int d = 0; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, S>(t, kb, wave, lane, d);
+  for (int d = 0; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V>(t, kb, st, wave, lane, d);
 }
 
 __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, uint32_t off1) {
@@ -228,102 +229,209 @@ struct BlockRegs {
   float ratio[C::MS];
 };
 
-// LDS reads and scale math of the K block in stage S: all A fragments, the
-// first kBBuf - 1 B fragments, the E8M0 exponents and the mantissa ratios.
-// off0/off1: this lane's byte offsets of its two 16-byte slots inside a 16-row
-// fragment (the same for A and B fragments).  mant: per-row mantissa product
-// the accumulator is expressed in (carried across K blocks).
-template <class C, int V, int S>
-__device__ __forceinline__ void load_block(BlockRegs<C>& r, float (&mant)[C::MS], uint32_t off0, uint32_t off1,
-                                           int wr, int wc, int r16) {
-  DG_LAS uint8_t* la = lds_a<C, V, S>() + wr * C::WM * kKBlock;
-  DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
-  DG_LAS float* ls = lds_s<C, V, S>();
-  const float sb = ls[(C::kWaves - 1) * 64 + C::kSAPerWave + (wc * C::WN) / 128];
+// Compile-time loop: f(std::integral_constant<int, I>) for I = I0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Raw scales of the K block in stage st that this lane needs: the wave's B
+// scale and the A scale of its row in each 16-row sub-tile.
+template <class C, int V>
+__device__ __forceinline__ void read_scales(float& sb, float (&sa)[C::MS], int st, int wr, int wc, int r16) {
+  DG_LAS float* ls = lds_s<C, V>(st);
+  sb = ls[(C::kWaves - 1) * 64 + C::kSAPerWave + (wc * C::WN) / 128];
 #pragma unroll
-  for (int ms = 0; ms < C::MS; ++ms) r.af[ms] = read_frag(la + ms * 16 * kKBlock, off0, off1);
-#pragma unroll
-  for (int t = 0; t < C::kBBuf - 1 && t < C::NS; ++t) r.bf[t] = read_frag(lb + t * 16 * kKBlock, off0, off1);
+  for (int ms = 0; ms < C::MS; ++ms) {
+    const int row = wr * C::WM + ms * 16 + r16;
+    sa[ms] = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
+  }
+}
+
+// E8M0 exponents and accumulator rescale ratios of a K block from its raw
+// scales.  mant: per-row mantissa product the accumulator is expressed in
+// (carried across K blocks).
+// keep: leave mant unchanged (the block is not used; its registers are).
+template <class C>
+__device__ __forceinline__ void scale_math(BlockRegs<C>& r, float (&mant)[C::MS], float sb, const float (&sa)[C::MS],
+                                           bool keep = false) {
   r.eb = scale_exponent(sb);
   const float mb = scale_mantissa(sb);
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
-    const int row = wr * C::WM + ms * 16 + r16;
-    const float sa = ls[(row / C::kSAPerWave) * 64 + row % C::kSAPerWave];
-    r.ea[ms] = scale_exponent(sa);
-    const float m = scale_mantissa(sa) * mb;
+    r.ea[ms] = scale_exponent(sa[ms]);
+    const float m = scale_mantissa(sa[ms]) * mb;
     r.ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
-    mant[ms] = m;
+    mant[ms] = keep ? mant[ms] : m;
   }
 }
 
-// MFMAs j in [J0, J1) of the K block in stage S.  Order: B fragment t = j / MS
-// outer, A fragment ms = j % MS inner; B fragment t + kBBuf - 1 is read while
-// t is used.  Each accumulator is rescaled two MFMAs before its own: its 4
-// multiplies are issued after MFMA j - 2, so that MFMA j does not wait out the
-// VALU-write -> MFMA-read hazard on its accumulator.  With DMA, this wave's DMA instructions for a later K block (kbd
-// into stage SD) are spread over the range, one every kDmaGap MFMAs (issued
-// back to back they would hold the wave at the address unit), the rest after
-// it.  No branches in the DMA: past the last K block the caller passes the
-// last block again (a harmless reload into a free stage).  sched_barrier(0)
-// between the groups keeps this order.
-template <class C, int V, int S, int SD, int J0, int J1, bool DMA>
-__device__ __forceinline__ void mfma_range(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r, uint32_t off0,
-                                           uint32_t off1, int wc, const TileSrc<C>& tsrc, int kbd, int wave,
-                                           int lane) {
-  constexpr int kN = J1 - J0;
-  constexpr int kDmaGap = kN / C::kLoadsPerStage > 0 ? kN / C::kLoadsPerStage : 1;
-  constexpr int kBBuf = C::kBBuf;
-  DG_LAS uint8_t* lb = lds_b<C, V, S>() + wc * C::WN * kKBlock;
-  rescale(acc[J0 % C::MS][J0 / C::MS], r.ratio[J0 % C::MS]);
-  if constexpr (J0 + 1 < J1) rescale(acc[(J0 + 1) % C::MS][(J0 + 1) / C::MS], r.ratio[(J0 + 1) % C::MS]);
-#pragma unroll
-  for (int j = J0; j < J1; ++j) {
-    __builtin_amdgcn_sched_barrier(0);
-    const int t = j / C::MS, ms = j % C::MS;
-    // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
-    // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
-    acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.bf[t % kBBuf], r.af[ms], acc[ms][t], 0, 0,
-                                                                  0, r.eb, 0, r.ea[ms]);
-    if (j + 2 < J1) {
-      const int t2 = (j + 2) / C::MS, ms2 = (j + 2) % C::MS;
-      rescale(acc[ms2][t2], r.ratio[ms2]);
-    }
-    const int tn = t + kBBuf - 1;
-    if (ms == 0 && tn < C::NS) r.bf[tn % kBBuf] = read_frag(lb + tn * 16 * kKBlock, off0, off1);
-    if constexpr (DMA) {
-      if ((j - J0) % kDmaGap == 0 && (j - J0) / kDmaGap < C::kLoadsPerStage)
-        issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, (j - J0) / kDmaGap);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (DMA && kN / kDmaGap < C::kLoadsPerStage) {
-#pragma unroll
-    for (int d = kN / kDmaGap; d < C::kLoadsPerStage; ++d) issue_dma_part<C, V, SD>(tsrc, kbd, wave, lane, d);
-  }
+// off0/off1: this lane's byte offsets of its two 16-byte slots inside a 16-row
+// fragment (the same for A and B fragments).
+template <class C, int V>
+__device__ __forceinline__ i32x8 read_a(int ms, int st, int wr, uint32_t off0, uint32_t off1) {
+  return read_frag(lds_a<C, V>(st) + (wr * C::WM + ms * 16) * kKBlock, off0, off1);
+}
+template <class C, int V>
+__device__ __forceinline__ i32x8 read_b(int t, int st, int wc, uint32_t off0, uint32_t off1) {
+  return read_frag(lds_b<C, V>(st) + (wc * C::WN + t * 16) * kKBlock, off0, off1);
 }
 
-// Every step issues one DMA group, so kStages - 2 younger groups may stay in
-// flight when a wave waits for its DMA of the block it is about to read.
+// All register state of the K block in stage 0 (first block of a tile).
+template <class C, int V>
+__device__ __forceinline__ void load_block(BlockRegs<C>& r, float (&mant)[C::MS], uint32_t off0, uint32_t off1,
+                                           int wr, int wc, int r16) {
+  float sb, sa[C::MS];
+  read_scales<C, V>(sb, sa, 0, wr, wc, r16);
+#pragma unroll
+  for (int ms = 0; ms < C::MS; ++ms) r.af[ms] = read_a<C, V>(ms, 0, wr, off0, off1);
+#pragma unroll
+  for (int t = 0; t < C::kBBuf - 1; ++t) r.bf[t] = read_b<C, V>(t, 0, wc, off0, off1);
+  scale_math(r, mant, sb, sa);
+}
+
+// Pipeline of one K block kb (stage S = kb % kStages).  MFMA j: B fragment
+// t = j / MS outer, A fragment ms = j % MS inner; B fragment t + kBBuf - 1 is
+// read while t is used.  The block's last MS MFMAs (fragment NS - 1) form the
+// tail.  After the tail's first MFMA every LDS read of stage S is done, so the
+// wave waits for its DMA of kb + 1 and passes the block barrier B(kb+1): every
+// wave's DMA of kb + 1 has landed and every wave is done reading stage S.  The
+// rest of the tail then reads block kb + 1's scales, first B fragments and A
+// fragments into the registers the tail frees (A fragment ms right after its
+// last MFMA), and starts the DMA of block kb + kStages into stage S.  That DMA
+// is finished in the head of the next step, one instruction per MFMA.  The
+// next block's first MFMA therefore finds its operands loaded: the barrier and
+// the LDS latency overlap the tail MFMAs.
+//
+// DMA accounting: block x's DMA (kLoadsPerStage instructions per wave) is
+// issued in the tail of step x - kStages and the head of step x - kStages + 1;
+// a tile's first kStages - 1 blocks and the tail part of block kStages - 1 come
+// from the tile prologue.  At B(y) every block before y + kStages - 1 has been
+// fully issued, so kStages - 2 younger blocks may stay in flight.  Past the
+// tile's last block the DMA re-loads the last block (a harmless reload into a
+// free stage) so that every count stays the same.
+template <class C>
+struct Pipe {
+  static constexpr int kJB = C::kMfmas - C::MS;                     // first tail MFMA
+  static constexpr int kTailDma = (C::MS - 1 < C::kLoadsPerStage) ? C::MS - 1 : C::kLoadsPerStage;
+  static constexpr int kHeadDma = C::kLoadsPerStage - kTailDma;
+  // With two stages the head part must land within this same block: issue it
+  // early, one instruction per MFMA; with more stages spread it out.
+  static constexpr int kHeadSpan = C::kStages == 2 ? (kHeadDma < kJB + 1 ? kHeadDma : kJB + 1) : kJB + 1;
+  static constexpr int kHeadGap = kHeadDma > 0 && kHeadSpan / kHeadDma > 0 ? kHeadSpan / kHeadDma : 1;
+  static_assert(C::NS % C::kBBuf == 0, "the tail's B fragment must not share a slot with the prefetched ones");
+};
+
 template <class C>
 __device__ __forceinline__ void wait_block_dma() {
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage>::value);
 }
 
-// One K block kb in LDS stage S = kb % kStages (all waves in step): wait for our
-// DMA of kb, barrier (every wave's DMA of kb landed; every wave is done reading
-// the stage kb-1 used), then compute kb while the DMA of kb + kStages - 1 is
-// issued into that freed stage.
-template <class C, int V, int S>
-__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS],
-                                     BlockRegs<C>& r, int kb, int kblocks, int wave, int lane, uint32_t off0,
-                                     uint32_t off1, int wr, int wc, int r16) {
+// One MFMA of the block: acc[ms][t] += 2^(eb + ea[ms]) * (B frag t) x (A frag ms),
+// then the accumulator two MFMAs ahead is rescaled to this block's mantissa
+// (its 4 multiplies run while this MFMA executes, and that MFMA does not wait
+// out the VALU-write -> MFMA-read hazard).
+template <class C, int J>
+__device__ __forceinline__ void mfma_one(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r) {
+  constexpr int t = J / C::MS, ms = J % C::MS;
+  // A port <- B rows (n), B port <- A rows (m): result lane l, reg r is
+  // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
+  acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.bf[t % C::kBBuf], r.af[ms], acc[ms][t], 0, 0, 0,
+                                                                r.eb, 0, r.ea[ms]);
+  if constexpr (J + 2 < C::kMfmas) rescale(acc[(J + 2) % C::MS][(J + 2) / C::MS], r.ratio[(J + 2) % C::MS]);
+}
+
+// Head of step kb (stage st): MFMAs 0 .. kJB, the head part of block kbd's DMA
+// into stage sd, and the streamed B fragment reads.
+template <class C, int V>
+__device__ __forceinline__ void head(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r, int st, int sd, uint32_t off0,
+                                     uint32_t off1, int wc, const TileSrc<C>& tsrc, int kbd, int wave, int lane) {
+  using P = Pipe<C>;
+  rescale(acc[0][0], r.ratio[0]);
+  if constexpr (C::kMfmas > 1) rescale(acc[1 % C::MS][1 / C::MS], r.ratio[1 % C::MS]);
+  static_for<0, P::kJB + 1>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_one<C, J>(acc, r);
+    constexpr int t = J / C::MS, ms = J % C::MS, tn = t + C::kBBuf - 1;
+    if constexpr (ms == 0 && tn < C::NS) r.bf[tn % C::kBBuf] = read_b<C, V>(tn, st, wc, off0, off1);
+    if constexpr (J % P::kHeadGap == 0 && J / P::kHeadGap < P::kHeadDma)
+      issue_dma_part<C, V>(tsrc, kbd, sd, wave, lane, P::kTailDma + J / P::kHeadGap);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr ((P::kJB + 1 + P::kHeadGap - 1) / P::kHeadGap < P::kHeadDma) {
+#pragma unroll
+    for (int d = (P::kJB + 1 + P::kHeadGap - 1) / P::kHeadGap; d < P::kHeadDma; ++d)
+      issue_dma_part<C, V>(tsrc, kbd, sd, wave, lane, P::kTailDma + d);
+  }
+}
+
+// Tail of step kb (next block's stage SN): barrier B(kb+1), prefetch of block
+// kb+1 into the freed registers, tail part of block kbd's DMA into S.  The
+// tile's last block runs the same code (no branch in the pipeline: it would
+// cost the in-place accumulation its registers); its "next block" is whatever
+// stage SN holds, and last leaves the mantissa state alone.
+template <class C, int V>
+__device__ __forceinline__ void tail(f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], BlockRegs<C>& r, int st,
+                                     int sn, uint32_t off0, uint32_t off1, int wr, int wc, int r16,
+                                     const TileSrc<C>& tsrc, int kbd, int wave, int lane, bool last) {
+  using P = Pipe<C>;
   wait_block_dma<C>();
   lds_barrier();
-  const int kbd = kb + C::kStages - 1;
-  load_block<C, V, S>(r, mant, off0, off1, wr, wc, r16);
-  mfma_range<C, V, S, (S + C::kStages - 1) % C::kStages, 0, C::kMfmas, true>(
-      acc, r, off0, off1, wc, t, kbd < kblocks ? kbd : kblocks - 1, wave, lane);
+  float sb, sa[C::MS];
+  read_scales<C, V>(sb, sa, sn, wr, wc, r16);
+#pragma unroll
+  for (int t = 0; t < C::kBBuf - 1; ++t) r.bf[t] = read_b<C, V>(t, sn, wc, off0, off1);
+  r.af[0] = read_a<C, V>(0, sn, wr, off0, off1);
+  static_for<0, C::MS - 1>([&](auto uc) {
+    constexpr int U = decltype(uc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_one<C, P::kJB + 1 + U>(acc, r);
+    r.af[U + 1] = read_a<C, V>(U + 1, sn, wr, off0, off1);
+    if constexpr (U < P::kTailDma) issue_dma_part<C, V>(tsrc, kbd, st, wave, lane, U);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  scale_math(r, mant, sb, sa, last);
+}
+
+// One K block kb in stage st = kb % kStages (see Pipe).
+template <class C, int V>
+__device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS],
+                                     BlockRegs<C>& r, int kb, int st, int kblocks, int wave, int lane, uint32_t off0,
+                                     uint32_t off1, int wr, int wc, int r16) {
+  const int sn = st + 1 == C::kStages ? 0 : st + 1;   // stage of kb + 1
+  const int sp = st == 0 ? C::kStages - 1 : st - 1;   // stage of kb - 1 (freed at B(kb))
+  const int kbh = kb + C::kStages - 1;                 // block whose DMA head part goes into sp
+  head<C, V>(acc, r, st, sp, off0, off1, wc, t, kbh < kblocks ? kbh : kblocks - 1, wave, lane);
+  const int kbt = kb + C::kStages;                     // block whose DMA tail part goes into st
+  tail<C, V>(acc, mant, r, st, sn, off0, off1, wr, wc, r16, t, kbt < kblocks ? kbt : kblocks - 1, wave, lane,
+             kb + 1 >= kblocks);
+}
+
+// Tile prologue DMA (all stages free): blocks 0 .. kStages-2 in full and the
+// tail part of block kStages-1.
+template <class C, int V>
+__device__ __forceinline__ void tile_dma(const TileSrc<C>& t, int kblocks, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < C::kStages - 1; ++i) issue_dma<C, V>(t, i < kblocks ? i : kblocks - 1, i, wave, lane);
+  constexpr int kL = C::kStages - 1;
+#pragma unroll
+  for (int d = 0; d < Pipe<C>::kTailDma; ++d)
+    issue_dma_part<C, V>(t, kL < kblocks ? kL : kblocks - 1, kL, wave, lane, d);
+}
+
+// B(0) and block 0's registers.  Only younger instructions than block 0's DMA
+// may remain in flight: the rest of the prologue DMA, and possibly stores of
+// the previous tile (issued after it; waiting for some of them is harmless).
+template <class C, int V>
+__device__ __forceinline__ void tile_start(float (&mant)[C::MS], BlockRegs<C>& r, uint32_t off0, uint32_t off1,
+                                           int wr, int wc, int r16) {
+  __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage + Pipe<C>::kTailDma>::value);
+  lds_barrier();
+  load_block<C, V>(r, mant, off0, off1, wr, wc, r16);
 }
 
 __device__ __forceinline__ int remap_for_xcd(int b, int grid) {
@@ -529,14 +637,8 @@ gemm_kernel(GemmParams p) {
       if (decode(tile, s)) break;
     return tile;
   };
-  // K blocks 0 .. kStages-2 into stages 0 .. kStages-2 (the last block again
-  // where the unit has fewer).
-  auto prologue = [&](const Tile& s) {
-#define DG_PROLOGUE(I) \
-    if constexpr (I < C::kStages - 1) issue_dma<C, V, I>(s.src, I < s.kbs ? I : s.kbs - 1, wave, lane);
-    DG_PROLOGUE(0) DG_PROLOGUE(1) DG_PROLOGUE(2) DG_PROLOGUE(3) DG_PROLOGUE(4) DG_PROLOGUE(5) DG_PROLOGUE(6)
-#undef DG_PROLOGUE
-  };
+  auto prologue = [&](const Tile& s) { tile_dma<C, V>(s.src, s.kbs, wave, lane); };
+
   // bf16 RNE, 16-byte stores of 8 consecutive columns.
   auto store_tile = [&](const Tile& s, f32x4 (&acc)[C::MS][C::NS]) {
     uint16_t* D = p.d + (V == kMasked ? (int64_t)s.g * p.d_gs : 0);
@@ -575,21 +677,15 @@ gemm_kernel(GemmParams p) {
       for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- main loop over K blocks, LDS stage = kb % kStages: whole periods of
-    // kStages blocks, then the remaining kbs % kStages blocks
+    // ---- main loop over K blocks, LDS stage = kb % kStages
     BlockRegs<C> r;
-    int kb = 0;
-#define DG_STEP(I) \
-    if constexpr (I < C::kStages) step<C, V, I>(cur.src, acc, mant, r, kb + I, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
-    for (; kb + C::kStages <= cur.kbs; kb += C::kStages) {
-      DG_STEP(0) DG_STEP(1) DG_STEP(2) DG_STEP(3) DG_STEP(4) DG_STEP(5) DG_STEP(6) DG_STEP(7)
+    tile_start<C, V>(mant, r, off0, off1, wr, wc, r16);
+    int st = 0;
+#pragma nounroll
+    for (int kb = 0; kb < cur.kbs; ++kb) {
+      step<C, V>(cur.src, acc, mant, r, kb, st, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
+      st = st + 1 == C::kStages ? 0 : st + 1;
     }
-#undef DG_STEP
-#define DG_TAIL(I)                     \
-    if constexpr (I < C::kStages - 1) \
-      if (kb + I < cur.kbs) step<C, V, I>(cur.src, acc, mant, r, kb + I, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
-    DG_TAIL(0) DG_TAIL(1) DG_TAIL(2) DG_TAIL(3) DG_TAIL(4) DG_TAIL(5) DG_TAIL(6)
-#undef DG_TAIL
 
     // ---- epilogue: back from mantissa units
 #pragma unroll

@@ -411,6 +411,24 @@ __device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C:
              kb + 1 >= kblocks);
 }
 
+// Step of a wave none of whose rows is written (rows past M, contiguous
+// padding, masked rows past masked_m): it issues its share of the tile's DMA
+// and passes the block barrier at the same points as step(), nothing else.
+template <class C, int V>
+__device__ __forceinline__ void idle_step(const TileSrc<C>& t, int kb, int st, int kblocks, int wave, int lane) {
+  using P = Pipe<C>;
+  const int sp = st == 0 ? C::kStages - 1 : st - 1;
+  const int kbh = kb + C::kStages - 1;
+#pragma unroll
+  for (int d = 0; d < P::kHeadDma; ++d)
+    issue_dma_part<C, V>(t, kbh < kblocks ? kbh : kblocks - 1, sp, wave, lane, P::kTailDma + d);
+  wait_block_dma<C>();
+  lds_barrier();
+  const int kbt = kb + C::kStages;
+#pragma unroll
+  for (int d = 0; d < P::kTailDma; ++d) issue_dma_part<C, V>(t, kbt < kblocks ? kbt : kblocks - 1, st, wave, lane, d);
+}
+
 // Tile prologue DMA (all stages free): blocks 0 .. kStages-2 in full and the
 // tail part of block kStages-1.
 template <class C, int V>
@@ -423,15 +441,13 @@ __device__ __forceinline__ void tile_dma(const TileSrc<C>& t, int kblocks, int w
     issue_dma_part<C, V>(t, kL < kblocks ? kL : kblocks - 1, kL, wave, lane, d);
 }
 
-// B(0) and block 0's registers.  Only younger instructions than block 0's DMA
-// may remain in flight: the rest of the prologue DMA, and possibly stores of
-// the previous tile (issued after it; waiting for some of them is harmless).
-template <class C, int V>
-__device__ __forceinline__ void tile_start(float (&mant)[C::MS], BlockRegs<C>& r, uint32_t off0, uint32_t off1,
-                                           int wr, int wc, int r16) {
+// B(0).  Only younger instructions than block 0's DMA may remain in flight:
+// the rest of the prologue DMA, and possibly stores of the previous tile
+// (issued after it; waiting for some of them is harmless).
+template <class C>
+__device__ __forceinline__ void tile_wait() {
   __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<(C::kStages - 2) * C::kLoadsPerStage + Pipe<C>::kTailDma>::value);
   lds_barrier();
-  load_block<C, V>(r, mant, off0, off1, wr, wc, r16);
 }
 
 __device__ __forceinline__ int remap_for_xcd(int b, int grid) {
@@ -677,14 +693,24 @@ gemm_kernel(GemmParams p) {
       for (int j = 0; j < C::NS; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- main loop over K blocks, LDS stage = kb % kStages
-    BlockRegs<C> r;
-    tile_start<C, V>(mant, r, off0, off1, wr, wc, r16);
+    // ---- main loop over K blocks, LDS stage = kb % kStages.  A wave none of
+    // whose rows is written only keeps the DMA and barrier schedule.
+    tile_wait<C>();
     int st = 0;
+    if (__builtin_amdgcn_ballot_w64(cur.okmask != 0) != 0) {
+      BlockRegs<C> r;
+      load_block<C, V>(r, mant, off0, off1, wr, wc, r16);
 #pragma nounroll
-    for (int kb = 0; kb < cur.kbs; ++kb) {
-      step<C, V>(cur.src, acc, mant, r, kb, st, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
-      st = st + 1 == C::kStages ? 0 : st + 1;
+      for (int kb = 0; kb < cur.kbs; ++kb) {
+        step<C, V>(cur.src, acc, mant, r, kb, st, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
+        st = st + 1 == C::kStages ? 0 : st + 1;
+      }
+    } else {
+#pragma nounroll
+      for (int kb = 0; kb < cur.kbs; ++kb) {
+        idle_step<C, V>(cur.src, kb, st, cur.kbs, wave, lane);
+        st = st + 1 == C::kStages ? 0 : st + 1;
+      }
     }
 
     // ---- epilogue: back from mantissa units

@@ -215,6 +215,78 @@ dg_status dg_per_block_cast_fp8(const void* x, int64_t ldx,
                                 int64_t n, int64_t k, int ue8m0,
                                 void* stream);
 
+/*
+ * Packed UE8M0 scales (the exponent-only scale format; page "GitHub 推荐：DeepSeek
+ * 开源周最大黑马 DeepGEMM…", 可复用的模式与技巧 "UE8M0 int32 packing" and
+ * the SF dual path next to it; page ssnai.com DeepGEMM analysis, on the scale
+ * formats of the two GPU generations).
+ *
+ * Packed contract: a scale word is an int32 holding the 8-bit biased
+ * exponents e (value 2^(e-127)) of 4 consecutive K blocks, little-endian:
+ * byte j (bits 8j..8j+7) of word w belongs to K block 4w + j.  Bytes past the
+ * last K block are ignored.  e = 255 is not a scale (outside the contract).
+ *   SFA words: logically [rows, ceil(K/512)]; word (i, w) at sfa[i * sfa_sm + w * sfa_sk]
+ *   SFB words: logically [ceil(N/128), ceil(K/512)]; word (nb, w) at sfb[nb * sfb_sn + w * sfb_sk]
+ * Strides are in int32 elements.  With such scales each K block's product
+ * 2^(ea + eb - 254) * P is exact in the accumulator's exponent range, so these
+ * entry points run kernels without any per-block rescaling; with power-of-two
+ * fp32 scales the fp32 entry points give bit-identical results.
+ */
+
+/* Dense GEMM as dg_fp8_gemm_nt_ws (same workspace rules) with packed UE8M0 scales. */
+dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda,
+                               const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                               const void* b, int64_t ldb,
+                               const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                               void* d, int64_t ldd,
+                               int64_t m, int64_t n, int64_t k,
+                               void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Contiguous grouped GEMM as dg_m_grouped_fp8_gemm_nt_contiguous with packed
+ * UE8M0 scales (sfb_group_stride in int32 elements). */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, int64_t lda,
+                                                    const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                                    const void* b, int64_t ldb, int64_t b_group_stride,
+                                                    const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                                    int64_t sfb_group_stride,
+                                                    void* d, int64_t ldd,
+                                                    const int32_t* m_indices, int64_t m_total,
+                                                    int64_t n, int64_t k, int num_groups,
+                                                    void* stream);
+
+/* Masked grouped GEMM as dg_m_grouped_fp8_gemm_nt_masked with packed UE8M0
+ * scales (group strides in int32 elements). */
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, int64_t lda, int64_t a_group_stride,
+                                                const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                                int64_t sfa_group_stride,
+                                                const void* b, int64_t ldb, int64_t b_group_stride,
+                                                const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                                int64_t sfb_group_stride,
+                                                void* d, int64_t ldd, int64_t d_group_stride,
+                                                const int32_t* masked_m, int num_groups,
+                                                int64_t max_m, int64_t n, int64_t k,
+                                                int64_t expected_m,
+                                                void* stream);
+
+/*
+ * Scale transform fp32 -> packed UE8M0: for every row i and K block kb,
+ * e = biased exponent of sf(i, kb), plus 1 when any mantissa bit is set (the
+ * smallest power of two >= the scale, as the casts' ue8m0 mode), stored in
+ * byte kb % 4 of word (i, kb / 4); bytes past the last K block are 0.  Exact for
+ * power-of-two scales, which is what the casts produce with ue8m0 != 0.  Inputs
+ * must be positive normal fp32 no larger than 2^127 (other values are outside
+ * the contract).
+ *   sf   device, fp32 [rows, kblocks]: element (i, kb) at sf[i * sf_s0 + kb * sf_s1]
+ *   out  device, int32 [rows, ceil(kblocks/4)]: word (i, w) at out[i * out_s0 + w * out_s1]
+ * Errors: negative sizes/strides or null pointers -> DG_ERROR_INVALID_VALUE;
+ * pointers not 4-byte aligned -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_pack_ue8m0(const float* sf, int64_t sf_s0, int64_t sf_s1,
+                        int32_t* out, int64_t out_s0, int64_t out_s1,
+                        int64_t rows, int64_t kblocks,
+                        void* stream);
+
 /* Row alignment of each group's segment in the contiguous layout: 128.
  * (Page ssnai.com DeepGEMM analysis: the alignment query for contiguous MoE.) */
 int dg_get_mk_alignment_for_contiguous_layout(void);

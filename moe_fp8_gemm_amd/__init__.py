@@ -9,11 +9,14 @@ importing this package fails loudly when the library has not been built.
 Tensor conventions (torch): E4M3 operands are ``torch.float8_e4m3fn`` (or
 ``torch.uint8`` holding the codes), scales ``torch.float32`` with any
 non-negative strides, outputs ``torch.bfloat16``.  Operands and scales are
-passed as pairs ``(codes, scales)``.
+passed as pairs ``(codes, scales)``.  The GEMMs also take packed UE8M0 scales
+(``torch.int32`` words holding the exponents of 4 consecutive K blocks, see
+``pack_ue8m0``): when both scale tensors are int32 the packed entry points run.
 """
 from __future__ import annotations
 
 import ctypes
+import itertools
 import os
 from typing import Optional, Tuple
 
@@ -49,6 +52,14 @@ _SIGNATURES = {
                            _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
     "dg_fp8_gemm_nt_workspace_size": ([_i64, _i64, _i64], ctypes.c_size_t),
     "dg_fp8_gemm_nt_tile_config": ([_i64, _i64, _i64, ctypes.c_size_t, _p, _p, _p], _i32),
+    "dg_fp8_gemm_nt_ue8m0": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
+                              _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": ([_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                   _i64, _p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64,
+                                               _i64, _i64, _p, _i64, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+                                              _i32),
+    "dg_pack_ue8m0": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p], _i32),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -88,9 +99,16 @@ def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _scales(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype != torch.float32 or not t.is_cuda:
-        raise TypeError(f"{name} must be a float32 device tensor")
+    if t.dtype not in (torch.float32, torch.int32) or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 (or packed UE8M0 int32) device tensor")
     return t
+
+
+def _packed(sa: torch.Tensor, sb: torch.Tensor) -> bool:
+    """True for packed UE8M0 scales (both int32), False for fp32 (both float32)."""
+    if sa.dtype != sb.dtype:
+        raise TypeError("sfa and sfb must both be float32 or both be packed int32")
+    return sa.dtype == torch.int32
 
 
 def _out_bf16(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -154,9 +172,10 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise TypeError("workspace must be a contiguous device tensor")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.dg_fp8_gemm_nt_ws(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
-                                 qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
-                                 d.data_ptr(), d.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream()),
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if _packed(sa, sb) else lib.dg_fp8_gemm_nt_ws
+    _check(fn(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+              qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
+              d.data_ptr(), d.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream()),
            "dg_fp8_gemm_nt")
     return d
 
@@ -173,7 +192,8 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     g, n, _ = qb.shape
     if qb.shape[2] != k or d.shape != (m_total, n) or m_indices.shape != (m_total,) or m_indices.stride(0) != 1:
         raise ValueError("shape mismatch")
-    _check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(
+    fn = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if _packed(sa, sb) else lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    _check(fn(
         qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
         qb.data_ptr(), qb.stride(1), qb.stride(0),
         sb.data_ptr(), sb.stride(1), sb.stride(2), sb.stride(0),
@@ -195,7 +215,8 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor,
     n = qb.shape[1]
     if qb.shape != (g, n, k) or d.shape != (g, max_m, n) or masked_m.shape != (g,):
         raise ValueError("shape mismatch")
-    _check(lib.dg_m_grouped_fp8_gemm_nt_masked(
+    fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if _packed(sa, sb) else lib.dg_m_grouped_fp8_gemm_nt_masked
+    _check(fn(
         qa.data_ptr(), qa.stride(1), qa.stride(0),
         sa.data_ptr(), sa.stride(1), sa.stride(2), sa.stride(0),
         qb.data_ptr(), qb.stride(1), qb.stride(0),
@@ -242,6 +263,28 @@ def per_block_cast_fp8(w: torch.Tensor, ue8m0: bool = False, q: Optional[torch.T
                                      sf.stride(0), sf.stride(1), n, k, int(bool(ue8m0)), _stream()),
            "per_block_cast_fp8")
     return q, sf
+
+
+def pack_ue8m0(sf: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 scales [..., rows, kblocks] -> packed UE8M0 int32 words [..., rows, ceil(kblocks/4)].
+
+    Byte j of word w is the biased exponent of scale 4w+j rounded up to a power of
+    two (exact for the power-of-two scales the casts produce with ``ue8m0=True``).
+    Leading dimensions (e.g. groups) are handled one matrix at a time; any strides.
+    """
+    if sf.dtype != torch.float32 or not sf.is_cuda or sf.dim() < 2:
+        raise TypeError("sf must be a float32 device tensor of at least 2 dims")
+    rows, kb = sf.shape[-2], sf.shape[-1]
+    words = (kb + 3) // 4
+    if out is None:
+        out = torch.empty(sf.shape[:-1] + (words,), dtype=torch.int32, device=sf.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != tuple(sf.shape[:-1]) + (words,) or not out.is_cuda:
+        raise ValueError("out must be an int32 device tensor of shape [..., rows, ceil(kblocks/4)]")
+    for idx in itertools.product(*(range(x) for x in sf.shape[:-2])):
+        s, o = sf[idx], out[idx]
+        _check(lib.dg_pack_ue8m0(s.data_ptr(), s.stride(0), s.stride(1), o.data_ptr(), o.stride(0), o.stride(1),
+                                 rows, kb, _stream()), "dg_pack_ue8m0")
+    return out
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

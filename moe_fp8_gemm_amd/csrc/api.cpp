@@ -39,8 +39,8 @@ int device_cus() { return g_num_cus_override > 0 ? g_num_cus_override : hw_cus()
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Checks shared by the three GEMM variants.
-dg_status check_common(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
-                       const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+dg_status check_common(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                       const void* b, int64_t ldb, const void* sfb, int64_t sfb_sn, int64_t sfb_sk,
                        const void* d, int64_t ldd, int64_t n, int64_t k) {
   if (!a || !b || !d || !sfa || !sfb) return DG_ERROR_INVALID_VALUE;
   if (n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
@@ -223,10 +223,15 @@ DG_EXPORT dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, 
   return DG_SUCCESS;
 }
 
-DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
-                                      const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
-                                      void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* ws,
-                                      size_t ws_bytes, void* stream) {
+namespace {
+
+// Scale words of either format are 4 bytes: the kernels take them through the
+// same pointers, the format selects how a K block finds its scale.
+const float* sf_ptr(const void* p) { return static_cast<const float*>(p); }
+
+dg_status gemm_nt(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk, const void* b,
+                  int64_t ldb, const void* sfb, int64_t sfb_sn, int64_t sfb_sk, void* d, int64_t ldd, int64_t m,
+                  int64_t n, int64_t k, void* ws, size_t ws_bytes, void* stream, bool packed) {
   if (m < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
   if (m == 0 || n == 0) return DG_SUCCESS;
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
@@ -235,11 +240,12 @@ DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* s
   if (ws && !aligned(ws, 16)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
-  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
+  p.sfa = sf_ptr(sfa); p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
   p.b = static_cast<const uint8_t*>(b); p.ldb = ldb;
-  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
+  p.sfb = sf_ptr(sfb); p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
+  p.sf_packed = packed ? 1 : 0;
   // The plan (and so the summation order) follows the hardware CU count, never
   // the grid-width override, so results do not depend on the override.  A
   // split plan runs only when the caller's workspace holds it.
@@ -256,6 +262,24 @@ DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* s
   return launch(plan.inst, kDense, p, plan.tiles, static_cast<hipStream_t>(stream));
 }
 
+}  // namespace
+
+DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                      const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                      void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return gemm_nt(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, m, n, k, ws, ws_bytes, stream,
+                 false);
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t sfa_sm,
+                                         int64_t sfa_sk, const void* b, int64_t ldb, const int32_t* sfb,
+                                         int64_t sfb_sn, int64_t sfb_sk, void* d, int64_t ldd, int64_t m, int64_t n,
+                                         int64_t k, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_nt(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, m, n, k, ws, ws_bytes, stream,
+                 true);
+}
+
 DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
                                    const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
                                    void* d, int64_t ldd, int64_t m, int64_t n, int64_t k, void* stream) {
@@ -263,12 +287,13 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
                            stream);
 }
 
-DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
-    const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
-    const void* b, int64_t ldb, int64_t b_group_stride,
-    const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
-    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
-    int64_t n, int64_t k, int num_groups, void* stream) {
+namespace {
+
+dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                             const void* b, int64_t ldb, int64_t b_group_stride, const void* sfb, int64_t sfb_sn,
+                             int64_t sfb_sk, int64_t sfb_group_stride, void* d, int64_t ldd,
+                             const int32_t* m_indices, int64_t m_total, int64_t n, int64_t k, int num_groups,
+                             void* stream, bool packed) {
   if (m_total < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
   if (b_group_stride < 0 || sfb_group_stride < 0) return DG_ERROR_INVALID_VALUE;
   if (m_total % kContiguousAlignment != 0) return DG_ERROR_MISALIGNED_LAYOUT;
@@ -280,26 +305,48 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
   if (!offsets_fit(m_total, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
-  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
+  p.sfa = sf_ptr(sfa); p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
   p.b = static_cast<const uint8_t*>(b); p.ldb = ldb; p.b_gs = b_group_stride;
-  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
+  p.sfb = sf_ptr(sfb); p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
   p.m_indices = m_indices;
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
+  p.sf_packed = packed ? 1 : 0;
   const GemmInstance inst = choose_contiguous(m_total, n, device_cus());
   const InstanceInfo info = instance_info(inst);
   const int64_t tiles = (m_total / info.bm) * ceil_div(n, info.bn);
   return launch(inst, kContiguous, p, tiles, static_cast<hipStream_t>(stream));
 }
 
-DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
-    const void* a, int64_t lda, int64_t a_group_stride,
-    const float* sfa, int64_t sfa_sm, int64_t sfa_sk, int64_t sfa_group_stride,
+}  // namespace
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
+    const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
     const void* b, int64_t ldb, int64_t b_group_stride,
     const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
-    void* d, int64_t ldd, int64_t d_group_stride,
-    const int32_t* masked_m, int num_groups, int64_t max_m, int64_t n, int64_t k,
-    int64_t expected_m, void* stream) {
+    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
+    int64_t n, int64_t k, int num_groups, void* stream) {
+  return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, stream, false);
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
+    const void* a, int64_t lda, const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
+    int64_t n, int64_t k, int num_groups, void* stream) {
+  return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, stream, true);
+}
+
+namespace {
+
+dg_status grouped_masked(const void* a, int64_t lda, int64_t a_group_stride, const void* sfa, int64_t sfa_sm,
+                         int64_t sfa_sk, int64_t sfa_group_stride, const void* b, int64_t ldb, int64_t b_group_stride,
+                         const void* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride, void* d,
+                         int64_t ldd, int64_t d_group_stride, const int32_t* masked_m, int num_groups, int64_t max_m,
+                         int64_t n, int64_t k, int64_t expected_m, void* stream, bool packed) {
   (void)expected_m;   // a size hint; results never depend on it
   if (max_m < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
   if (a_group_stride < 0 || sfa_group_stride < 0 || b_group_stride < 0 || sfb_group_stride < 0 ||
@@ -315,18 +362,47 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
   if (!offsets_fit(max_m, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda; p.a_gs = a_group_stride;
-  p.sfa = sfa; p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk; p.sfa_gs = sfa_group_stride;
+  p.sfa = sf_ptr(sfa); p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk; p.sfa_gs = sfa_group_stride;
   p.b = static_cast<const uint8_t*>(b); p.ldb = ldb; p.b_gs = b_group_stride;
-  p.sfb = sfb; p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
+  p.sfb = sf_ptr(sfb); p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk; p.sfb_gs = sfb_group_stride;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd; p.d_gs = d_group_stride;
   p.masked_m = masked_m;
   p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
+  p.sf_packed = packed ? 1 : 0;
   // Masked decode streams each group's B once per M tile: a 256-row tile covers
   // groups of up to 256 rows in one pass.
   const GemmInstance inst = max_m > 128 ? kInstHuge : kInstLarge;
   const InstanceInfo info = instance_info(inst);
   const int64_t bound = (int64_t)num_groups * ceil_div(max_m, info.bm) * ceil_div(n, info.bn);
   return launch(inst, kMasked, p, bound, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked(
+    const void* a, int64_t lda, int64_t a_group_stride,
+    const float* sfa, int64_t sfa_sm, int64_t sfa_sk, int64_t sfa_group_stride,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, int64_t d_group_stride,
+    const int32_t* masked_m, int num_groups, int64_t max_m, int64_t n, int64_t k,
+    int64_t expected_m, void* stream) {
+  return grouped_masked(a, lda, a_group_stride, sfa, sfa_sm, sfa_sk, sfa_group_stride, b, ldb, b_group_stride, sfb,
+                        sfb_sn, sfb_sk, sfb_group_stride, d, ldd, d_group_stride, masked_m, num_groups, max_m, n, k,
+                        expected_m, stream, false);
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(
+    const void* a, int64_t lda, int64_t a_group_stride,
+    const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk, int64_t sfa_group_stride,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, int64_t d_group_stride,
+    const int32_t* masked_m, int num_groups, int64_t max_m, int64_t n, int64_t k,
+    int64_t expected_m, void* stream) {
+  return grouped_masked(a, lda, a_group_stride, sfa, sfa_sm, sfa_sk, sfa_group_stride, b, ldb, b_group_stride, sfb,
+                        sfb_sn, sfb_sk, sfb_group_stride, d, ldd, d_group_stride, masked_m, num_groups, max_m, n, k,
+                        expected_m, stream, true);
 }
 
 namespace {
@@ -374,6 +450,17 @@ DG_EXPORT dg_status dg_per_block_cast_fp8(const void* x, int64_t ldx, void* q, i
   if (ceil_div(n, 128) * (k / 128) > INT_MAX) return DG_ERROR_NOT_SUPPORTED;
   CastParams p{x, ldx, static_cast<uint8_t*>(q), ldq, sf, sf_sn, sf_sk, n, k, ue8m0 ? 1 : 0};
   return launch_per_block_cast(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
+}
+
+DG_EXPORT dg_status dg_pack_ue8m0(const float* sf, int64_t sf_s0, int64_t sf_s1, int32_t* out, int64_t out_s0,
+                                  int64_t out_s1, int64_t rows, int64_t kblocks, void* stream) {
+  if (rows < 0 || kblocks < 0 || sf_s0 < 0 || sf_s1 < 0 || out_s0 < 0 || out_s1 < 0) return DG_ERROR_INVALID_VALUE;
+  if (rows == 0 || kblocks == 0) return DG_SUCCESS;
+  if (!sf || !out) return DG_ERROR_INVALID_VALUE;
+  if (!aligned(sf, 4) || !aligned(out, 4)) return DG_ERROR_NOT_SUPPORTED;
+  PackParams p{sf, sf_s0, sf_s1, out, out_s0, out_s1, rows, kblocks};
+  return launch_pack_ue8m0(p, device_cus(), static_cast<hipStream_t>(stream)) == hipSuccess ? DG_SUCCESS
+                                                                                            : DG_ERROR_LAUNCH;
 }
 
 DG_EXPORT int dg_get_mk_alignment_for_contiguous_layout(void) { return kContiguousAlignment; }

@@ -174,7 +174,41 @@ __global__ void __launch_bounds__(256) per_block_cast_kernel(CastParams p) {
   if (threadIdx.x == 0) p.sf[nb * p.sf_s0 + kb * p.sf_s1] = d.s;
 }
 
+// Packing of power-of-two scales into UE8M0 words: byte j of word (i, w) is
+// the biased fp32 exponent of scale (i, 4w + j) rounded up to a power of two
+// (the exponent plus one when any mantissa bit is set), 0 past the last K
+// block.  One thread per word; a scale that already is a power of two keeps
+// its exact value.  (Page "GitHub 推荐…DeepGEMM…", 可复用的模式与技巧: four
+// UE8M0 exponents per int32, little-endian.)
+__global__ void __launch_bounds__(256) pack_ue8m0_kernel(PackParams p) {
+  const int64_t words = (p.kblocks + 3) / 4;
+  const int64_t total = p.rows * words;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / words, w = i - r * words;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kb = 4 * w + j;
+      if (kb < p.kblocks) {
+        const uint32_t bits = __builtin_bit_cast(uint32_t, p.sf[r * p.sf_s0 + kb * p.sf_s1]);
+        const uint32_t e = ((bits >> 23) & 0xFFu) + ((bits & 0x7FFFFFu) != 0u ? 1u : 0u);
+        word |= (e & 0xFFu) << (8 * j);
+      }
+    }
+    p.out[r * p.out_s0 + w * p.out_s1] = (int32_t)word;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_ue8m0(const PackParams& p, int num_cus, hipStream_t stream) {
+  const int64_t total = p.rows * ((p.kblocks + 3) / 4);
+  int64_t grid = (total + 255) / 256;
+  const int64_t cap = (int64_t)num_cus * 16;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(pack_ue8m0_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus, hipStream_t stream) {
   int64_t grid = (p.rows + 3) / 4;               // one row per wave

@@ -36,6 +36,9 @@ struct GemmParams {
   int* counters;
   int splits;
   int kb_per_split;
+  // scale format: 0 = fp32 scales, 1 = packed UE8M0 (int32 words holding the
+  // exponents of 4 consecutive K blocks; sfa/sfb then point at those words)
+  int sf_packed;
 };
 
 // Kernel instances the host can pick (see gemm_fp8.hip for the tile shapes).
@@ -45,7 +48,6 @@ enum GemmInstance : int {
   kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
   kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves (small M, usually split over K)
   kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves (M <= 64, usually split over K)
-  kInstMidPair = 5,   // 128 x 128 output tiles, 8 waves, 2-stage pipeline, two workgroups per CU
   kNumInstances
 };
 
@@ -72,5 +74,15 @@ struct CastParams {
 hipError_t launch_per_token_cast(const CastParams& p, bool input_fp32, int num_cus,
                                  hipStream_t stream);
 hipError_t launch_per_block_cast(const CastParams& p, hipStream_t stream);
+
+// fp32 scales -> packed UE8M0 words (see dg_pack_ue8m0).
+struct PackParams {
+  const float* sf;
+  int64_t sf_s0, sf_s1;           // element (i, kb) at sf[i * sf_s0 + kb * sf_s1]
+  int32_t* out;
+  int64_t out_s0, out_s1;         // word (i, w) at out[i * out_s0 + w * out_s1]
+  int64_t rows, kblocks;
+};
+hipError_t launch_pack_ue8m0(const PackParams& p, int num_cus, hipStream_t stream);
 
 }  // namespace dgfp8

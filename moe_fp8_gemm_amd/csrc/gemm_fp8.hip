@@ -107,6 +107,7 @@ struct Cfg {
   static constexpr int kStages = STAGES_;   // LDS stages; K blocks in flight = kStages - 1
   static constexpr int kBBuf = BBUF_;       // B fragments held in registers (streamed)
   static constexpr int kOcc = OCC_;         // workgroups resident per CU
+  static constexpr bool kPackedSf = false;  // scales: fp32 (false) or packed UE8M0 (see SfCfg)
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -129,6 +130,16 @@ struct Cfg {
   static_assert(NS % 2 == 0, "epilogue stores 8 columns at a time");
   static_assert(kStages >= 2 && kStages <= 8, "pipeline depth");
   static_assert((kStages - 2) * kLoadsPerStage <= 63, "vmcnt range of the stage wait");
+};
+
+// A tile configuration whose scales come as packed UE8M0 exponents: one int32
+// holds the 8-bit biased exponents of 4 consecutive K blocks, little-endian
+// (page "GitHub 推荐…DeepGEMM…", 可复用的模式与技巧, UE8M0 int32 packing).  An
+// exponent byte is exactly the block-scaled MFMA's E8M0 scale operand, so these
+// kernels have no mantissa arithmetic at all: no rescale, no epilogue factor.
+template <class Base, bool kPacked>
+struct SfCfg : Base {
+  static constexpr bool kPackedSf = kPacked;
 };
 
 // LDS buffers, one array of kStages stages per (config, variant, kind): every
@@ -157,8 +168,9 @@ struct TileSrc {
   const uint8_t* b_base;
   uint32_t a_off[C::kAChunksPerWave];
   uint32_t b_off[C::kBChunksPerWave];
-  const float* s_src;       // this lane's scale at K block 0 (A row scale or B block scale)
+  const float* s_src;       // this lane's scale word at K block 0 (A row scale or B block scale)
   int64_t s_kstride;
+  int kb0;                  // absolute index of the unit's first K block (split-K), for packed scales
 };
 
 // DMA instruction d (0 <= d < kLoadsPerStage) of this wave's share of K block kb
@@ -173,7 +185,10 @@ __device__ __forceinline__ void issue_dma_part(const TileSrc<C>& t, int kb, int 
     const int j = d - NA;
     dma16(t.b_base + (int64_t)kb * kKBlock, t.b_off[j], lds_addr(lds_b<C, V>(st)) + (wave * NB + j) * 1024);
   } else {
-    dma4(t.s_src + kb * t.s_kstride, lds_addr(lds_s<C, V>(st)) + wave * 64 * 4);
+    // fp32: one word per K block (s_src already points at the unit's first
+    // block); packed: one word per 4 K blocks, indexed by the absolute block.
+    const int64_t w = C::kPackedSf ? (int64_t)((t.kb0 + kb) >> 2) : (int64_t)kb;
+    dma4(t.s_src + w * t.s_kstride, lds_addr(lds_s<C, V>(st)) + wave * 64 * 4);
   }
 }
 
@@ -255,9 +270,17 @@ __device__ __forceinline__ void read_scales(float& sb, float (&sa)[C::MS], int s
 // scales.  mant: per-row mantissa product the accumulator is expressed in
 // (carried across K blocks).
 // keep: leave mant unchanged (the block is not used; its registers are).
+// kb_abs: absolute K block index (selects the byte of a packed scale word).
 template <class C>
 __device__ __forceinline__ void scale_math(BlockRegs<C>& r, float (&mant)[C::MS], float sb, const float (&sa)[C::MS],
-                                           bool keep = false) {
+                                           int kb_abs, bool keep = false) {
+  if constexpr (C::kPackedSf) {
+    const int sh = (kb_abs & 3) * 8;
+    r.eb = (int)((__builtin_bit_cast(uint32_t, sb) >> sh) & 0xFFu);
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms) r.ea[ms] = (int)((__builtin_bit_cast(uint32_t, sa[ms]) >> sh) & 0xFFu);
+    return;
+  }
   r.eb = scale_exponent(sb);
   const float mb = scale_mantissa(sb);
 #pragma unroll
@@ -283,14 +306,14 @@ __device__ __forceinline__ i32x8 read_b(int t, int st, int wc, uint32_t off0, ui
 // All register state of the K block in stage 0 (first block of a tile).
 template <class C, int V>
 __device__ __forceinline__ void load_block(BlockRegs<C>& r, float (&mant)[C::MS], uint32_t off0, uint32_t off1,
-                                           int wr, int wc, int r16) {
+                                           int wr, int wc, int r16, int kb_abs) {
   float sb, sa[C::MS];
   read_scales<C, V>(sb, sa, 0, wr, wc, r16);
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) r.af[ms] = read_a<C, V>(ms, 0, wr, off0, off1);
 #pragma unroll
   for (int t = 0; t < C::kBBuf - 1; ++t) r.bf[t] = read_b<C, V>(t, 0, wc, off0, off1);
-  scale_math(r, mant, sb, sa);
+  scale_math(r, mant, sb, sa, kb_abs);
 }
 
 // Pipeline of one K block kb (stage S = kb % kStages).  MFMA j: B fragment
@@ -341,7 +364,8 @@ __device__ __forceinline__ void mfma_one(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C
   // D[m = row l%16 of A fragment ms][n = row 4*(l/16)+r of B fragment t].
   acc[ms][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.bf[t % C::kBBuf], r.af[ms], acc[ms][t], 0, 0, 0,
                                                                 r.eb, 0, r.ea[ms]);
-  if constexpr (J + 2 < C::kMfmas) rescale(acc[(J + 2) % C::MS][(J + 2) / C::MS], r.ratio[(J + 2) % C::MS]);
+  if constexpr (!C::kPackedSf && J + 2 < C::kMfmas)
+    rescale(acc[(J + 2) % C::MS][(J + 2) / C::MS], r.ratio[(J + 2) % C::MS]);
 }
 
 // Head of step kb (stage st): MFMAs 0 .. kJB, the head part of block kbd's DMA
@@ -350,8 +374,10 @@ template <class C, int V>
 __device__ __forceinline__ void head(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r, int st, int sd, uint32_t off0,
                                      uint32_t off1, int wc, const TileSrc<C>& tsrc, int kbd, int wave, int lane) {
   using P = Pipe<C>;
-  rescale(acc[0][0], r.ratio[0]);
-  if constexpr (C::kMfmas > 1) rescale(acc[1 % C::MS][1 / C::MS], r.ratio[1 % C::MS]);
+  if constexpr (!C::kPackedSf) {
+    rescale(acc[0][0], r.ratio[0]);
+    if constexpr (C::kMfmas > 1) rescale(acc[1 % C::MS][1 / C::MS], r.ratio[1 % C::MS]);
+  }
   static_for<0, P::kJB + 1>([&](auto jc) {
     constexpr int J = decltype(jc)::value;
     __builtin_amdgcn_sched_barrier(0);
@@ -377,7 +403,7 @@ __device__ __forceinline__ void head(f32x4 (&acc)[C::MS][C::NS], BlockRegs<C>& r
 template <class C, int V>
 __device__ __forceinline__ void tail(f32x4 (&acc)[C::MS][C::NS], float (&mant)[C::MS], BlockRegs<C>& r, int st,
                                      int sn, uint32_t off0, uint32_t off1, int wr, int wc, int r16,
-                                     const TileSrc<C>& tsrc, int kbd, int wave, int lane, bool last) {
+                                     const TileSrc<C>& tsrc, int kbd, int wave, int lane, bool last, int kb_next) {
   using P = Pipe<C>;
   wait_block_dma<C>();
   lds_barrier();
@@ -394,7 +420,7 @@ __device__ __forceinline__ void tail(f32x4 (&acc)[C::MS][C::NS], float (&mant)[C
     if constexpr (U < P::kTailDma) issue_dma_part<C, V>(tsrc, kbd, st, wave, lane, U);
   });
   __builtin_amdgcn_sched_barrier(0);
-  scale_math(r, mant, sb, sa, last);
+  scale_math(r, mant, sb, sa, tsrc.kb0 + kb_next, last);
 }
 
 // One K block kb in stage st = kb % kStages (see Pipe).
@@ -408,7 +434,7 @@ __device__ __forceinline__ void step(const TileSrc<C>& t, f32x4 (&acc)[C::MS][C:
   head<C, V>(acc, r, st, sp, off0, off1, wc, t, kbh < kblocks ? kbh : kblocks - 1, wave, lane);
   const int kbt = kb + C::kStages;                     // block whose DMA tail part goes into st
   tail<C, V>(acc, mant, r, st, sn, off0, off1, wr, wc, r16, t, kbt < kblocks ? kbt : kblocks - 1, wave, lane,
-             kb + 1 >= kblocks);
+             kb + 1 >= kblocks, kb + 1);
 }
 
 // Step of a wave none of whose rows is written (rows past M, contiguous
@@ -574,6 +600,7 @@ gemm_kernel(GemmParams p) {
 
       // ---- DMA sources: uniform bases, per-lane 32-bit offsets (host checks they fit)
       TileSrc<C>& t = s.src;
+      t.kb0 = 0;
       t.a_base = p.a + (V == kMasked ? (int64_t)g * p.a_gs : 0);
       t.b_base = p.b + (V != kDense ? (int64_t)g * p.b_gs : 0);
 #pragma unroll
@@ -625,7 +652,8 @@ gemm_kernel(GemmParams p) {
         kbs = min(p.kb_per_split, kblocks - kb0);
         t.a_base += (int64_t)kb0 * kKBlock;
         t.b_base += (int64_t)kb0 * kKBlock;
-        t.s_src += (int64_t)kb0 * t.s_kstride;
+        if constexpr (!C::kPackedSf) t.s_src += (int64_t)kb0 * t.s_kstride;
+        t.kb0 = kb0;
       }
     // All of these are wave-uniform; say so, so that they stay in scalar
     // registers across the tile loop.
@@ -699,7 +727,7 @@ gemm_kernel(GemmParams p) {
     int st = 0;
     if (__builtin_amdgcn_ballot_w64(cur.okmask != 0) != 0) {
       BlockRegs<C> r;
-      load_block<C, V>(r, mant, off0, off1, wr, wc, r16);
+      load_block<C, V>(r, mant, off0, off1, wr, wc, r16, cur.src.kb0);
 #pragma nounroll
       for (int kb = 0; kb < cur.kbs; ++kb) {
         step<C, V>(cur.src, acc, mant, r, kb, st, cur.kbs, wave, lane, off0, off1, wr, wc, r16);
@@ -714,10 +742,12 @@ gemm_kernel(GemmParams p) {
     }
 
     // ---- epilogue: back from mantissa units
+    if constexpr (!C::kPackedSf) {
 #pragma unroll
-    for (int ms = 0; ms < C::MS; ++ms)
+      for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-      for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
+        for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
+    }
     Tile nxt;
     const int ntile = next_tile(tile + gridDim.x, nxt);
     if constexpr (V == kDenseSplitK) {
@@ -796,11 +826,10 @@ using CfgSkinny128 = Cfg<128, 64, 4, 2, 3>;
 using CfgSkinny64 = Cfg<64, 64, 4, 2, 3>;
 using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
-using CfgMidPair = Cfg<128, 128, 4, 2, 2, 2, 2>;   // two workgroups per CU
 
 // Variants compiled per configuration: bit v of Mask set = variant v available.
 template <class C, int Mask>
-hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stream) {
+hipError_t launch_variant(Variant v, const GemmParams& p, int grid, hipStream_t stream) {
   dim3 block(C::kThreads);
   if (!((Mask >> v) & 1)) return hipErrorInvalidValue;
   switch (v) {
@@ -822,6 +851,12 @@ hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stre
   return hipGetLastError();
 }
 
+template <class C, int Mask>
+hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stream) {
+  return p.sf_packed ? launch_variant<SfCfg<C, true>, Mask>(v, p, grid, stream)
+                     : launch_variant<C, Mask>(v, p, grid, stream);
+}
+
 constexpr int kAll = (1 << kDense) | (1 << kContiguous) | (1 << kMasked) | (1 << kDenseSplitK);
 constexpr int kDenseAndSplit = (1 << kDense) | (1 << kDenseSplitK);
 
@@ -834,7 +869,6 @@ InstanceInfo instance_info(GemmInstance inst) {
     case kInstSkinny64: return {CfgSkinny64::BM, CfgSkinny64::BN, CfgSkinny64::kOcc};
     case kInstLarge: return {CfgLarge::BM, CfgLarge::BN, CfgLarge::kOcc};
     case kInstMid: return {CfgMid::BM, CfgMid::BN, CfgMid::kOcc};
-    case kInstMidPair: return {CfgMidPair::BM, CfgMidPair::BN, CfgMidPair::kOcc};
     default: return {0, 0};
   }
 }
@@ -846,7 +880,6 @@ hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int gr
     case kInstSkinny64: return launch_cfg<CfgSkinny64, kDenseAndSplit>(v, p, grid, stream);
     case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);
     case kInstMid: return launch_cfg<CfgMid, kAll>(v, p, grid, stream);
-    case kInstMidPair: return launch_cfg<CfgMidPair, kAll>(v, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,8 +14,9 @@ Modules:
 * ``gemm``  -- dense, M-grouped contiguous and M-grouped masked references:
   decode exactly, scale per K block, accumulate in float64, round once.
 * ``exact`` -- the same GEMM in exact rational arithmetic, for tiny shapes.
+* ``ue8m0`` -- packing of exponent-only scales, four per int32 word.
 
 Every function is pinned by CPU tests against closed forms, library decoders,
 brute force and invariants; no function is "parity unpinned".
 """
-from . import bf16, e4m3, exact, gemm, quant  # noqa: F401
+from . import bf16, e4m3, exact, gemm, quant, ue8m0  # noqa: F401

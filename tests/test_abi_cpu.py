@@ -139,3 +139,28 @@ def test_cast_validation(lib):
     assert f(P, i(512), P, i(512), P, i(4), i(1), i(0), i(512), 0, None) == 0
     g = lib.dg_per_block_cast_fp8
     assert g(P, i(512), P, i(512), P, i(4), i(1), i(8), i(100), 0, None) == 2
+
+
+def test_packed_scale_entries_validation(lib):
+    i = ctypes.c_int64
+    f = lib.dg_fp8_gemm_nt_ue8m0
+
+    def call(a=P, lda=512, sfa=P, b=P, sfb=P, d=P, m=128, n=256, k=512, ws=None, ws_bytes=0):
+        return f(a, i(lda), sfa, i(1), i(128), b, i(512), sfb, i(1), i(2), d, i(256), i(m), i(n), i(k),
+                 ws, ctypes.c_size_t(ws_bytes), None)
+
+    assert call(sfa=None) == 1
+    assert call(k=500) == 2
+    assert call(m=0) == 0
+    assert call(ws=ctypes.c_void_p(0x10004), ws_bytes=1 << 20) == 2       # misaligned workspace
+    c = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0
+    assert c(P, i(512), P, i(1), i(256), P, i(512), i(1 << 20), P, i(2), i(1), i(4), P, i(256), P, i(200),
+             i(256), i(512), 4, None) == 3                                # m_total % 128
+    mk = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0
+    assert mk(P, i(512), i(1 << 20), P, i(1), i(256), i(1024), P, i(512), i(1 << 20), P, i(2), i(1), i(4),
+              P, i(256), i(1 << 16), None, 4, i(256), i(256), i(512), i(128), None) == 1   # masked_m null
+    pk = lib.dg_pack_ue8m0
+    assert pk(None, i(4), i(1), P, i(1), i(1), i(8), i(4), None) == 1
+    assert pk(P, i(4), i(1), ctypes.c_void_p(0x10002), i(1), i(1), i(8), i(4), None) == 2
+    assert pk(P, i(-1), i(1), P, i(1), i(1), i(8), i(4), None) == 1
+    assert pk(P, i(4), i(1), P, i(1), i(1), i(0), i(4), None) == 0

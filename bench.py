@@ -60,6 +60,18 @@ def make_dense(dg, m, n, k, seed, dev):
     return (qa, sa), (qb, sb), d
 
 
+def packed_mn_major(dg, sf, dev, groups=None):
+    """Packed UE8M0 words of power-of-two fp32 scales [..., rows, kblocks], in the
+    MN-major layout for A: word (row, w) at w * rows + row."""
+    rows, kb = sf.shape[-2], sf.shape[-1]
+    words = (kb + 3) // 4
+    if groups is None:
+        out = torch.empty((words, rows), dtype=torch.int32, device=dev).t()
+    else:
+        out = torch.empty((groups, words, rows), dtype=torch.int32, device=dev).transpose(1, 2)
+    return dg.pack_ue8m0(sf, out=out)
+
+
 class Flusher:
     """Reads a 1 GiB buffer so that cold-cache timings do not see operands left in
     the 256 MB Infinity Cache (MALL) or the L2s.  It reads rather than writes: a
@@ -136,6 +148,30 @@ def bench_extras(dg, dev, reps):
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS,
             "b_read_gbs": b_bytes / ms / 1e6}
         del qa, sa, qb, sb, d
+    # --- dense M=4096 shapes with power-of-two scales: fp32 scale words vs packed UE8M0 words
+    shapes4k = [s for s in synth.config1_shapes() if s[0] == 4096]
+    tot_flops, t_fp32, t_packed = 0.0, 0.0, 0.0
+    per = {}
+    for (m, n, k) in shapes4k:
+        seed = synth.seed_for(1, synth.config1_shapes().index((m, n, k)))
+        a32 = synth.draw_activation_device(m, k, seed, dev)
+        b32 = synth.draw_weight_device(n, k, seed, 0, dev)
+        qa, sa = dg.per_token_cast_fp8(a32, ue8m0=True, sf=mn_major(m, k // 128, dev))
+        qb, sb = dg.per_block_cast_fp8(b32, ue8m0=True)
+        del a32, b32
+        pa, pb = packed_mn_major(dg, sa, dev), dg.pack_ue8m0(sb)
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ms_f = event_time_ms(lambda: dg.fp8_gemm_nt((qa, sa), (qb, sb), d), reps, flush)
+        ms_p = event_time_ms(lambda: dg.fp8_gemm_nt((qa, pa), (qb, pb), d), reps, flush)
+        f = 2.0 * m * n * k
+        tot_flops += f
+        t_fp32 += ms_f
+        t_packed += ms_p
+        per[f"{m}x{n}x{k}"] = {"us_fp32_scales": ms_f * 1e3, "us_packed_ue8m0": ms_p * 1e3}
+        del qa, sa, qb, sb, pa, pb, d
+    out["dense_M4096_pow2_scales"] = {
+        "tflops_fp32_scales": tot_flops / t_fp32 / 1e9, "tflops_packed_ue8m0": tot_flops / t_packed / 1e9,
+        "pct_fp8_peak_packed_ue8m0": 100 * tot_flops / t_packed / 1e9 / FP8_PEAK_TFLOPS, "per_shape": per}
     # --- Zipf contiguous G=256, power-of-two scales
     counts, m_indices = synth.config4_routing()
     n, k = synth.CONFIG4_NK
@@ -153,11 +189,16 @@ def bench_extras(dg, dev, reps):
     d = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
     mi = torch.from_numpy(m_indices).to(dev)
     ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi), max(3, reps // 2), flush)
+    pa, pb = packed_mn_major(dg, sa, dev), dg.pack_ue8m0(sb)
+    ms_p = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, pa), (qb, pb), d, mi), max(3, reps // 2),
+                         flush)
     useful = 2.0 * int(counts.sum()) * n * k
     out["contiguous_zipf_G256_4096x7168_ue8m0"] = {
         "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
         "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "b_read_gbs": 256 * n * k / ms / 1e6,
-        "m_total": m_total}
+        "m_total": m_total, "us_packed_ue8m0_scales": ms_p * 1e3,
+        "tflops_useful_packed_ue8m0": useful / ms_p / 1e9}
+    del pa, pb
     del qa, sa, qb, sb, d
     # --- per-token cast of the bf16 activation
     x = synth.config4_cast_input().to(dev)

@@ -108,6 +108,27 @@ dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda,
                             void* ws, size_t ws_bytes,
                             void* stream);
 
+/*
+ * Accumulating dense GEMM: D = RNE_bf16(C + A . B^T), C an fp32 addend of D's
+ * shape added to the fp32 result before the single rounding to bf16.  The
+ * optional c argument of fp8_gemm_nt (page "GitHub 推荐…DeepGEMM…", 解法哲学);
+ * the pages say no more about it, and this reading is the plainest one.
+ * Same arguments, workspace rules and results as dg_fp8_gemm_nt_ws, plus
+ *   c    device, fp32 [m, n], row stride ldc (elements); read only, must not
+ *        overlap d
+ * Errors (for m, n > 0): null c or ldc < n -> DG_ERROR_INVALID_VALUE;
+ * c not 16-byte aligned or ldc % 4 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_fp8_gemm_nt_acc(const void* a, int64_t lda,
+                             const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                             const void* b, int64_t ldb,
+                             const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                             const float* c, int64_t ldc,
+                             void* d, int64_t ldd,
+                             int64_t m, int64_t n, int64_t k,
+                             void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Workspace bytes dg_fp8_gemm_nt_ws needs to split this problem; 0 when the
  * problem runs unsplit (or the sizes are invalid).  Depends only on m, n, k
  * and the device's compute-unit count. */

@@ -60,6 +60,8 @@ _SIGNATURES = {
                                                _i64, _i64, _p, _i64, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
                                               _i32),
     "dg_pack_ue8m0": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p], _i32),
+    "dg_fp8_gemm_nt_acc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
+                            _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -148,13 +150,14 @@ def _auto_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
 
 
 def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
-                d: torch.Tensor, workspace=_AUTO) -> torch.Tensor:
-    """d[m, n] = bf16( A . B^T ) with per-(row, 128-K) A scales and per-128x128 B scales.
+                d: torch.Tensor, c: Optional[torch.Tensor] = None, workspace=_AUTO) -> torch.Tensor:
+    """d[m, n] = bf16( A . B^T [+ c] ) with per-(row, 128-K) A scales and per-128x128 B scales.
 
     a = (codes [m, k], sfa [m, k/128]); b = (codes [n, k], sfb [ceil(n/128), k/128]);
-    d bf16 [m, n] is overwritten and returned.  ``workspace``: "auto" (a cached
-    per-device buffer, enabling split-K for small m), None (never split), or a
-    zero-initialised uint8 device tensor of at least ``workspace_size(m, n, k)`` bytes.
+    d bf16 [m, n] is overwritten and returned; c, when given, is an fp32 [m, n]
+    addend (fp32 scales only).  ``workspace``: "auto" (a cached per-device buffer,
+    enabling split-K for small m), None (never split), or a zero-initialised uint8
+    device tensor of at least ``workspace_size(m, n, k)`` bytes.
     """
     (qa, sa), (qb, sb) = a, b
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
@@ -172,7 +175,18 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise TypeError("workspace must be a contiguous device tensor")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    fn = lib.dg_fp8_gemm_nt_ue8m0 if _packed(sa, sb) else lib.dg_fp8_gemm_nt_ws
+    packed = _packed(sa, sb)
+    if c is not None:
+        if packed:
+            raise NotImplementedError("the accumulating GEMM takes fp32 scales")
+        if c.dtype != torch.float32 or not c.is_cuda or c.shape != (m, n) or c.stride(1) != 1:
+            raise TypeError("c must be a float32 device tensor [m, n] with unit column stride")
+        _check(lib.dg_fp8_gemm_nt_acc(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+                                      qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
+                                      c.data_ptr(), c.stride(0), d.data_ptr(), d.stride(0), m, n, k,
+                                      ws_ptr or None, ws_bytes, _stream()), "dg_fp8_gemm_nt_acc")
+        return d
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if packed else lib.dg_fp8_gemm_nt_ws
     _check(fn(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
               qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
               d.data_ptr(), d.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream()),

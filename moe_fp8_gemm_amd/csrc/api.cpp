@@ -231,7 +231,8 @@ const float* sf_ptr(const void* p) { return static_cast<const float*>(p); }
 
 dg_status gemm_nt(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk, const void* b,
                   int64_t ldb, const void* sfb, int64_t sfb_sn, int64_t sfb_sk, void* d, int64_t ldd, int64_t m,
-                  int64_t n, int64_t k, void* ws, size_t ws_bytes, void* stream, bool packed) {
+                  int64_t n, int64_t k, void* ws, size_t ws_bytes, void* stream, bool packed,
+                  const float* c = nullptr, int64_t ldc = 0) {
   if (m < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
   if (m == 0 || n == 0) return DG_SUCCESS;
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
@@ -244,6 +245,7 @@ dg_status gemm_nt(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, i
   p.b = static_cast<const uint8_t*>(b); p.ldb = ldb;
   p.sfb = sf_ptr(sfb); p.sfb_sn = sfb_sn; p.sfb_sk = sfb_sk;
   p.d = static_cast<uint16_t*>(d); p.ldd = ldd;
+  p.c = c; p.ldc = ldc;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   p.sf_packed = packed ? 1 : 0;
   // The plan (and so the summation order) follows the hardware CU count, never
@@ -270,6 +272,18 @@ DG_EXPORT dg_status dg_fp8_gemm_nt_ws(const void* a, int64_t lda, const float* s
                                       size_t ws_bytes, void* stream) {
   return gemm_nt(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, m, n, k, ws, ws_bytes, stream,
                  false);
+}
+
+DG_EXPORT dg_status dg_fp8_gemm_nt_acc(const void* a, int64_t lda, const float* sfa, int64_t sfa_sm,
+                                       int64_t sfa_sk, const void* b, int64_t ldb, const float* sfb, int64_t sfb_sn,
+                                       int64_t sfb_sk, const float* c, int64_t ldc, void* d, int64_t ldd, int64_t m,
+                                       int64_t n, int64_t k, void* ws, size_t ws_bytes, void* stream) {
+  if (m > 0 && n > 0) {
+    if (!c || ldc < n) return DG_ERROR_INVALID_VALUE;
+    if (ldc % 4 != 0 || !aligned(c, 16)) return DG_ERROR_NOT_SUPPORTED;
+  }
+  return gemm_nt(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, m, n, k, ws, ws_bytes, stream,
+                 false, c, ldc);
 }
 
 DG_EXPORT dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t sfa_sm,

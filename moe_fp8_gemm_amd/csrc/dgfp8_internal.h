@@ -25,6 +25,8 @@ struct GemmParams {
   int64_t sfb_sn, sfb_sk, sfb_gs;
   uint16_t* d;
   int64_t ldd, d_gs;
+  const float* c;                 // dense only: fp32 addend [m, n] (row stride ldc), or null
+  int64_t ldc;
   const int32_t* m_indices;       // contiguous
   const int32_t* masked_m;        // masked
   int64_t m;                      // dense: M, contiguous: m_total, masked: max_m

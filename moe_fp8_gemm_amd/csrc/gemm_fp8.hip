@@ -683,7 +683,8 @@ gemm_kernel(GemmParams p) {
   };
   auto prologue = [&](const Tile& s) { tile_dma<C, V>(s.src, s.kbs, wave, lane); };
 
-  // bf16 RNE, 16-byte stores of 8 consecutive columns.
+  // bf16 RNE, 16-byte stores of 8 consecutive columns; dense variants add the
+  // optional fp32 addend C first (D = C + A.B^T, rounded once).
   auto store_tile = [&](const Tile& s, f32x4 (&acc)[C::MS][C::NS]) {
     uint16_t* D = p.d + (V == kMasked ? (int64_t)s.g * p.d_gs : 0);
     const int er16 = lane & 15, eq = lane >> 4;
@@ -696,8 +697,15 @@ gemm_kernel(GemmParams p) {
       for (int j = 0; j < C::NS / 2; ++j) {
         const int64_t col = n0 + wc * C::WN + 32 * j + 8 * eq;
         if (col < p.n) {
-          const f32x4 x0 = acc[ms][2 * j];
-          const f32x4 x1 = acc[ms][2 * j + 1];
+          f32x4 x0 = acc[ms][2 * j];
+          f32x4 x1 = acc[ms][2 * j + 1];
+          if constexpr (V == kDense || V == kDenseSplitK) {
+            if (p.c) {
+              const float* crow = p.c + (m0 + wr * C::WM + ms * 16 + er16) * p.ldc + col;
+              x0 += *(const f32x4*)crow;
+              x1 += *(const f32x4*)(crow + 4);
+            }
+          }
           u32x4 v;
           v.x = pack_bf16x2(x0[0], x0[1]);
           v.y = pack_bf16x2(x0[2], x0[3]);
@@ -786,14 +794,20 @@ gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < C::NS; ++j) acc[ms][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < p.splits; ++sp) {
+          // all of a split's loads first, then the adds: one wait, not one per load
+          f32x4 v[C::MS][C::NS];
 #pragma unroll
           for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
             for (int j = 0; j < C::NS; ++j)
 #pragma unroll
               for (int c = 0; c < 4; ++c)
-                acc[ms][j][c] += __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v[ms][j][c] = __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+            for (int j = 0; j < C::NS; ++j) acc[ms][j] += v[ms][j];
         }
         // ready for the next call
         if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -810,8 +824,15 @@ gemm_kernel(GemmParams p) {
       // store this tile while they are in flight.
       __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
       lds_barrier();
-      if (ntile < num_tiles) prologue(nxt);
-      store_tile(cur, acc);
+      if ((V == kDense || V == kDenseSplitK) && p.c) {
+        // The addend's loads must come before the next tile's DMAs: a wait for
+        // them placed after those DMAs would wait for the DMAs too.
+        store_tile(cur, acc);
+        if (ntile < num_tiles) prologue(nxt);
+      } else {
+        if (ntile < num_tiles) prologue(nxt);
+        store_tile(cur, acc);
+      }
     }
     cur = nxt;
     tile = ntile;

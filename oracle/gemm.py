@@ -46,9 +46,19 @@ def gemm_nt_fp64(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarray)
     return a64 @ b64.T
 
 
-def gemm_nt(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarray) -> np.ndarray:
-    """Dense reference: bf16 bits uint16 [M, N]."""
-    return round_to_bf16_bits(gemm_nt_fp64(a, sfa, b, sfb))
+def gemm_nt(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarray,
+            c: Optional[np.ndarray] = None) -> np.ndarray:
+    """Dense reference: bf16 bits uint16 [M, N].
+
+    With ``c`` (fp32 [M, N]): D = RNE_bf16(C + A . B^T), the accumulating form of
+    the call (page "GitHub 推荐…DeepGEMM…", 解法哲学: the optional ``c`` argument
+    of fp8_gemm_nt; the pages give no more, and the reading taken is an fp32
+    addend of D's shape, added exactly before the single rounding).
+    """
+    acc = gemm_nt_fp64(a, sfa, b, sfb)
+    if c is not None:
+        acc = acc + np.asarray(c, dtype=np.float32).astype(np.float64)
+    return round_to_bf16_bits(acc)
 
 
 def gemm_nt_sampled(a: np.ndarray, sfa: np.ndarray, b: np.ndarray, sfb: np.ndarray,

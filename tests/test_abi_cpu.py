@@ -164,3 +164,18 @@ def test_packed_scale_entries_validation(lib):
     assert pk(P, i(4), i(1), ctypes.c_void_p(0x10002), i(1), i(1), i(8), i(4), None) == 2
     assert pk(P, i(-1), i(1), P, i(1), i(1), i(8), i(4), None) == 1
     assert pk(P, i(4), i(1), P, i(1), i(1), i(0), i(4), None) == 0
+
+
+def test_accumulate_entry_validation(lib):
+    i = ctypes.c_int64
+    f = lib.dg_fp8_gemm_nt_acc
+
+    def call(c=P, ldc=256, m=128, n=256):
+        return f(P, i(512), P, i(4), i(1), P, i(512), P, i(4), i(1), c, i(ldc), P, i(256), i(m), i(n), i(512),
+                 None, ctypes.c_size_t(0), None)
+
+    assert call(c=None) == 1
+    assert call(ldc=200) == 1                                  # ldc < n
+    assert call(ldc=258) == 2                                  # ldc % 4
+    assert call(c=ctypes.c_void_p(0x10008)) == 2               # c not 16-byte aligned
+    assert call(c=None, m=0) == 0                              # empty problem

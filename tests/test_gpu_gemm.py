@@ -89,6 +89,31 @@ def test_power_of_two_scale_linearity_bit_exact():
     assert np.array_equal(f(down), f(base) * np.float32(0.25))
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 520, 4096), (1, 8, 128), (256, 512, 1024)])
+def test_accumulate_parity(m, n, k):
+    # D = RNE_bf16(C + A.B^T); (64, 520, 4096) takes the split-K path, where the
+    # last unit to arrive adds C.
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + 2 * n + k)
+    rng = np.random.default_rng(m + n)
+    c = (rng.standard_normal((m, n)) * 4).astype(np.float32)
+    a, b = (upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb))
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d, c=upload(c))
+    torch.cuda.synchronize()
+    assert_gemm_close(bits(d), ogemm.gemm_nt(qa, sa, qb, sb, c), f"acc {m}x{n}x{k}")
+    # a zero addend gives the plain result bit for bit; a strided addend (ldc > n) works
+    plain = _gpu_dense(qa, sa, qb, sb)
+    d0 = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d0, c=torch.zeros((m, n), dtype=torch.float32, device=device()))
+    wide = torch.zeros((m, n + 12), dtype=torch.float32, device=device())
+    wide[:, :n] = upload(c)
+    d1 = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d1, c=wide[:, :n])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d0), plain)
+    assert np.array_equal(bits(d1), bits(d))
+
+
 @pytest.mark.parametrize("m,n,k", [(700, 1032, 768), (96, 1032, 3072)])
 def test_deterministic_and_independent_of_grid_width(m, n, k):
     qa, sa, qb, sb = _host_problem(m, n, k, seed=8)

@@ -213,3 +213,32 @@ def test_quantize_then_gemm_close_to_fp32_matmul():
     ref = w.a.astype(np.float64) @ w.b.astype(np.float64).T
     rel = np.linalg.norm(d - ref) / np.linalg.norm(ref)
     assert rel < 0.05
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_accumulate_form_matches_exact_rationals(seed):
+    # D = RNE_bf16(C + A.B^T): the fp32 addend enters the exact sum before the one rounding.
+    from fractions import Fraction
+    rng = np.random.default_rng(300 + seed)
+    m, n, k = int(rng.integers(1, 7)), int(rng.integers(1, 7)), 256
+    a, b = _random_codes(rng, (m, k)), _random_codes(rng, (n, k))
+    sfa, sfb = _random_scales(rng, (m, 2), bool(seed % 2)), _random_scales(rng, (1, 2), bool(seed % 2))
+    c = (rng.standard_normal((m, n)) * 1e4).astype(np.float32)
+    got = gemm.gemm_nt(a, sfa, b, sfb, c)
+    ex = exact.gemm_nt_exact(a, sfa, b, sfb)
+    for i in range(m):
+        for j in range(n):
+            total = ex[i][j] + Fraction(float(c[i, j]))
+            if not exact.is_bf16_tie(total):
+                assert int(got[i, j]) == exact.round_fraction_to_bf16_bits(total)
+
+
+def test_accumulate_special_cases():
+    rng = np.random.default_rng(7)
+    a, b = _random_codes(rng, (5, 384)), _random_codes(rng, (6, 384))
+    sfa, sfb = _random_scales(rng, (5, 3), False), _random_scales(rng, (1, 3), False)
+    assert np.array_equal(gemm.gemm_nt(a, sfa, b, sfb, np.zeros((5, 6), np.float32)), gemm.gemm_nt(a, sfa, b, sfb))
+    c = rng.standard_normal((5, 6)).astype(np.float32)
+    zero_a = np.zeros_like(a)
+    want = torch.from_numpy(c).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gemm.gemm_nt(zero_a, sfa, b, sfb, c), want)   # library fp32 -> bf16 RNE

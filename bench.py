@@ -10,9 +10,13 @@ whole-step TFLOPS (2*M*N*K summed over the step / wall time of K steps).
 
 The JSON line also carries:
 * ``roofline``: the dominant kernel (the tile/split instance that takes most of
-  the step), algorithmic FLOPs per launch / its average launch time
-  measured with HIP events on the launch stream inside the timed steps, against
-  the 5.0 PFLOP/s dense FP8 MFMA peak;
+  the step), algorithmic FLOPs per launch / its average launch time, against
+  the 5.0 PFLOP/s dense FP8 MFMA peak.  The launch time is measured inside the
+  timed steps with HIP events on the launch stream, one pair around each run of
+  consecutive launches of that instance (event time / launches).  Events
+  between launches cost GPU time, so the timed steps carry no others;
+* ``per_shape``: ``us_in_step`` from separate untimed steps with an event pair
+  around every launch, and cold-cache times (operands evicted before each run);
 * ``cpu_baseline``: the CPU oracle timed on the full 4096x4096x7168 GEMM (4 runs);
 * ``extras``: cold-cache per-shape times, the MoE workloads (contiguous G=8,
   masked G=16, Zipf contiguous G=256 with power-of-two scales) and the per-token
@@ -296,41 +300,76 @@ def main():
     torch.cuda.synchronize()
     flops = [2.0 * m * n * k for (m, n, k) in shapes]
 
-    def step(events=None):
+    # Which (tile, split) instance runs each launch: the plan is a pure function
+    # of the shape.  The dominant instance is the one that takes most of the step.
+    cfgs = [dg.tile_config(m, n, k) for (m, n, k) in shapes]
+
+    def step(marks=None):
+        """One pass over the workload.  marks: {launch index: (start event or
+        None, end event or None)} recorded around those launches only."""
         for i, (a, b, d) in enumerate(probs):
-            if events is not None:
-                events[i][0].record()
+            if marks and i in marks and marks[i][0] is not None:
+                marks[i][0].record()
             dg.fp8_gemm_nt(a, b, d)
-            if events is not None:
-                events[i][1].record()
+            if marks and i in marks and marks[i][1] is not None:
+                marks[i][1].record()
+
+    def new_event():
+        return torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in shapes] for _ in range(args.steps)]
+
+    # ---- per-launch times, from separate (untimed) steps with an event pair
+    # around every launch.  Events cost GPU time between launches, so the timed
+    # steps below carry only the few the roofline needs.
+    probe_steps = max(3, min(args.steps, 10))
+    probe = [{i: (new_event(), new_event()) for i in range(len(shapes))} for _ in range(probe_steps)]
+    for s in range(probe_steps):
+        step(probe[s])
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
-    per_launch = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(shapes))]
-                           for s in range(args.steps)])      # ms
+    per_launch = np.array([[probe[s][i][0].elapsed_time(probe[s][i][1]) for i in range(len(shapes))]
+                           for s in range(probe_steps)])      # ms
     mean_ms = per_launch.mean(axis=0)
-    # The dominant kernel: the (tile, split) instance that takes most of the step.
-    # Its achieved rate = algorithmic FLOPs per launch / average launch duration,
-    # both averaged over that instance's launches in the timed steps.
-    cfgs = [dg.tile_config(m, n, k) for (m, n, k) in shapes]
     by_cfg = {}
     for i, c in enumerate(cfgs):
         by_cfg.setdefault(c, []).append(i)
     dom_cfg = max(by_cfg, key=lambda c: sum(mean_ms[i] for i in by_cfg[c]))
     big = by_cfg[dom_cfg]
-    dom_time = float(mean_ms[big].mean())
+    # runs of consecutive launches of the dominant instance: one event pair per run
+    runs, cur = [], [big[0]]
+    for i in big[1:]:
+        if i == cur[-1] + 1:
+            cur.append(i)
+        else:
+            runs.append(cur)
+            cur = [i]
+    runs.append(cur)
+
+    # ---- timed steps: wall clock over the whole job; HIP events on the launch
+    # stream bracket each run of dominant-instance launches
+    log(f"timing {args.steps} steps")
+    marks = []
+    for _ in range(args.steps):
+        mk = {}
+        for r in runs:
+            e0, e1 = new_event(), new_event()
+            mk[r[0]] = (e0, mk.get(r[0], (None, None))[1])
+            mk[r[-1]] = (mk.get(r[-1], (None, None))[0], e1)
+        marks.append(mk)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(marks[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+    # The dominant kernel's achieved rate = algorithmic FLOPs per launch / average
+    # launch duration (event time of its runs over the timed steps / launches).
+    dom_total_ms = sum(marks[s][r[0]][0].elapsed_time(marks[s][r[-1]][1]) for s in range(args.steps) for r in runs)
+    dom_time = dom_total_ms / (args.steps * len(big))
     dom_flops = float(np.mean([flops[i] for i in big]))
     achieved = dom_flops / (dom_time * 1e-3) / 1e12
     if args.calib_copy:

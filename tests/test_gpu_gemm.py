@@ -129,6 +129,51 @@ def test_deterministic_and_independent_of_grid_width(m, n, k):
     assert_gemm_close(ref, ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
+# Several tiles per workgroup: 256x256 tiles (two LDS stages) with ragged M and
+# N edges and a last M tile whose waves are mostly idle, 128x256 tiles (three
+# stages) with three and with two K blocks (fewer blocks than stages).  A
+# narrow grid makes one or five workgroups walk all tiles in turn; the result
+# must not change.
+CHAINED = [(2600, 3104, 640, 256), (4100, 2056, 256, 256), (3000, 2504, 384, 128), (2048, 4096, 256, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,bm", CHAINED)
+def test_chained_tiles_on_a_narrow_grid(m, n, k, bm):
+    assert dg.tile_config(m, n, k)[0] == bm, "shape no longer picks this tile"
+    print(f"chained tiles {m}x{n}x{k}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + k)
+    ref = _gpu_dense(qa, sa, qb, sb)
+    assert_gemm_close(ref, ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
+    try:
+        for cus in (1, 5):
+            dg.set_num_cus(cus)
+            assert np.array_equal(ref, _gpu_dense(qa, sa, qb, sb)), cus
+    finally:
+        dg.set_num_cus(0)
+
+
+def test_chained_tiles_accumulate_on_a_narrow_grid():
+    m, n, k = 2600, 3104, 640
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=5)
+    c = np.random.default_rng(5).standard_normal((m, n)).astype(np.float32)
+    a = (upload_codes(qa), upload(sa))
+    b = (upload_codes(qb), upload(sb))
+
+    def run():
+        d = sentinel_like((m, n))
+        dg.fp8_gemm_nt(a, b, d, c=upload(c))
+        torch.cuda.synchronize()
+        return bits(d)
+
+    ref = run()
+    assert_gemm_close(ref, ogemm.gemm_nt(qa, sa, qb, sb, c), "acc chained")
+    try:
+        dg.set_num_cus(3)
+        assert np.array_equal(ref, run())
+    finally:
+        dg.set_num_cus(0)
+
+
 # Small M with deep K: the output has too few tiles for the device, so the K
 # blocks are split over several workgroups per output tile (partials summed in
 # split order by the last one to arrive).

@@ -76,6 +76,20 @@ def test_dense_packed_equals_fp32_path(m, n, k):
     assert_gemm_close(got, want, f"packed {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(2600, 3104, 640), (700, 1032, 768)])
+def test_dense_packed_chained_tiles(m, n, k):
+    """Workgroups walking many tiles in turn: each tile's first scale byte is
+    picked by its own block index (5 and 6 blocks per tile, not multiples of 4)."""
+    qa, sa, qb, sb = _dense_pow2(m, n, k, seed=k)
+    ref = _run_dense(qa, upload(sa), qb, upload(sb))
+    try:
+        for cus in (1, 3):
+            dg.set_num_cus(cus)
+            assert np.array_equal(_run_dense(qa, _pack(sa), qb, _pack(sb)), ref), cus
+    finally:
+        dg.set_num_cus(0)
+
+
 def test_dense_packed_mn_major_scale_words():
     qa, sa, qb, sb = _dense_pow2(300, 264, 1664, seed=9)          # 13 K blocks: a partial last word
     words = ue8m0.pack(sa)

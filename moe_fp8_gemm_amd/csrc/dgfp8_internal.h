@@ -48,8 +48,8 @@ enum GemmInstance : int {
   kInstLarge = 0,     // 128 x 256 output tiles, 8 waves, 3-stage LDS pipeline
   kInstMid = 1,       // 128 x 128 output tiles, 8 waves, 3-stage LDS pipeline
   kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
-  kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves (small M, usually split over K)
-  kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves (M <= 64, usually split over K)
+  kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves, 4-stage LDS pipeline (small M, usually split over K)
+  kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves, 4-stage LDS pipeline (M <= 64, usually split over K)
   kNumInstances
 };
 

@@ -843,8 +843,8 @@ gemm_kernel(GemmParams p) {
 }
 
 using CfgHuge = Cfg<256, 256, 4, 2, 2, 2>;
-using CfgSkinny128 = Cfg<128, 64, 4, 2, 3>;
-using CfgSkinny64 = Cfg<64, 64, 4, 2, 3>;
+using CfgSkinny128 = Cfg<128, 64, 4, 2, 4>;
+using CfgSkinny64 = Cfg<64, 64, 4, 2, 4>;
 using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
 

@@ -151,6 +151,14 @@ def bench_extras(dg, dev, reps):
         out[f"masked_G16_{n}x{k}"] = {
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS,
             "b_read_gbs": b_bytes / ms / 1e6}
+        # decode shape on the same operands: 0..32 rows per group, run on the
+        # 64-row decode tiles (hint 16) and on the 256-row tiles (hint 128)
+        mm_dec = torch.from_numpy(synth.masked_counts(16, 32, seed + 500)).to(dev)
+        ms_dec = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm_dec, 16), reps, flush)
+        ms_big = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm_dec, 128), reps, flush)
+        out[f"masked_decode_G16_{n}x{k}"] = {
+            "rows": int(mm_dec.sum().item()), "us_64row_tiles": ms_dec * 1e3, "us_256row_tiles": ms_big * 1e3,
+            "b_read_gbs_64row_tiles": b_bytes / ms_dec / 1e6, "b_read_gbs_256row_tiles": b_bytes / ms_big / 1e6}
         del qa, sa, qb, sb, d
     # --- dense M=4096 shapes with power-of-two scales: fp32 scale words vs packed UE8M0 words
     shapes4k = [s for s in synth.config1_shapes() if s[0] == 4096]

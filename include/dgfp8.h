@@ -182,7 +182,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, int64_t lda,
  *   d        device, bf16 [num_groups, max_m, n]; group g at d + g * d_group_stride, rows ldd
  *   masked_m device, int32 [num_groups]: valid rows of each group, read on the
  *            device at run time (never by the host), clamped to [0, max_m]
- *   expected_m  hint of the typical masked_m; never changes results
+ *   expected_m  hint of the typical masked_m (it picks the tile height: at most
+ *            64 selects 64-row tiles, made for decode); never changes results
  * For group g, rows i < masked_m[g] get A[g, i] times B[g]^T; rows at or beyond
  * masked_m[g] are left untouched.
  * Page juejin.cn, section 4(3) (masked grouped GEMM for decode with graphs).

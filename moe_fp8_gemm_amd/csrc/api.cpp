@@ -361,7 +361,6 @@ dg_status grouped_masked(const void* a, int64_t lda, int64_t a_group_stride, con
                          const void* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride, void* d,
                          int64_t ldd, int64_t d_group_stride, const int32_t* masked_m, int num_groups, int64_t max_m,
                          int64_t n, int64_t k, int64_t expected_m, void* stream, bool packed) {
-  (void)expected_m;   // a size hint; results never depend on it
   if (max_m < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
   if (a_group_stride < 0 || sfa_group_stride < 0 || b_group_stride < 0 || sfb_group_stride < 0 ||
       d_group_stride < 0)
@@ -383,9 +382,14 @@ dg_status grouped_masked(const void* a, int64_t lda, int64_t a_group_stride, con
   p.masked_m = masked_m;
   p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
   p.sf_packed = packed ? 1 : 0;
-  // Masked decode streams each group's B once per M tile: a 256-row tile covers
-  // groups of up to 256 rows in one pass.
-  const GemmInstance inst = max_m > 128 ? kInstHuge : kInstLarge;
+  // Each group's B is streamed once per M tile: a 256-row tile covers groups
+  // of up to 256 rows in one pass.  When the caller expects few rows per group
+  // (decode: expected_m <= 64), 64-row tiles stage a quarter of the A rows and
+  // leave LDS for a third stage.  expected_m is a hint only: every instance
+  // computes each output element with the same operations in the same order,
+  // so the results are the same bits whichever instance runs.
+  const GemmInstance inst = (expected_m > 0 && expected_m <= 64) ? kInstDecode
+                            : (max_m > 128 ? kInstHuge : kInstLarge);
   const InstanceInfo info = instance_info(inst);
   const int64_t bound = (int64_t)num_groups * ceil_div(max_m, info.bm) * ceil_div(n, info.bn);
   return launch(inst, kMasked, p, bound, static_cast<hipStream_t>(stream));

@@ -50,6 +50,7 @@ enum GemmInstance : int {
   kInstHuge = 2,      // 256 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, masked)
   kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves, 4-stage LDS pipeline (small M, usually split over K)
   kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves, 4-stage LDS pipeline (M <= 64, usually split over K)
+  kInstDecode = 5,    // 64 x 256 output tiles, 8 waves side by side, 3-stage LDS pipeline (masked, few rows)
   kNumInstances
 };
 

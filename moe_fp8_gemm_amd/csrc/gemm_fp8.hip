@@ -847,6 +847,8 @@ using CfgSkinny128 = Cfg<128, 64, 4, 2, 4>;
 using CfgSkinny64 = Cfg<64, 64, 4, 2, 4>;
 using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
+// Masked decode (few rows per group): one 64-row wave band across 256 columns.
+using CfgDecode = Cfg<64, 256, 1, 8, 3>;
 
 // Variants compiled per configuration: bit v of Mask set = variant v available.
 template <class C, int Mask>
@@ -890,6 +892,7 @@ InstanceInfo instance_info(GemmInstance inst) {
     case kInstSkinny64: return {CfgSkinny64::BM, CfgSkinny64::BN, CfgSkinny64::kOcc};
     case kInstLarge: return {CfgLarge::BM, CfgLarge::BN, CfgLarge::kOcc};
     case kInstMid: return {CfgMid::BM, CfgMid::BN, CfgMid::kOcc};
+    case kInstDecode: return {CfgDecode::BM, CfgDecode::BN, CfgDecode::kOcc};
     default: return {0, 0};
   }
 }
@@ -901,6 +904,7 @@ hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int gr
     case kInstSkinny64: return launch_cfg<CfgSkinny64, kDenseAndSplit>(v, p, grid, stream);
     case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);
     case kInstMid: return launch_cfg<CfgMid, kAll>(v, p, grid, stream);
+    case kInstDecode: return launch_cfg<CfgDecode, (1 << kMasked)>(v, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

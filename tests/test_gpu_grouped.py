@@ -173,11 +173,28 @@ def test_masked_parity_small_with_edge_counts():
             assert_gemm_close(got[g, :c], want[g, :c], f"masked group {g}")
 
 
-def test_masked_expected_m_is_only_a_hint():
-    qa, sa, qb, sb, masked_m = _masked_host(4, 130, 136, 256, seed=22, masked_m=[130, 3, 0, 77])
-    a = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=1)
-    b = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=4096)
-    assert np.array_equal(a, b)
+@pytest.mark.parametrize("max_m,counts", [(130, [130, 3, 0, 77]), (100, [100, 65, 64, 1])])
+def test_masked_expected_m_is_only_a_hint(max_m, counts):
+    """The hint picks the tile (64-row decode tiles up to 64, else 256- or
+    128-row tiles by max_m); the output bits must not change."""
+    qa, sa, qb, sb, masked_m = _masked_host(4, max_m, 136, 256, seed=22, masked_m=counts)
+    ref = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=1)
+    for hint in (64, 65, 128, 4096):
+        assert np.array_equal(ref, _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=hint)), hint
+
+
+def test_masked_decode_tiles_parity():
+    """Decode-shaped masked problem on the 64-row tiles: groups of 0..150 rows
+    (up to three 64-row tiles), N not a multiple of the 256-column tile."""
+    mm = [0, 1, 16, 63, 64, 65, 150]
+    qa, sa, qb, sb, masked_m = _masked_host(7, 256, 520, 1280, seed=23, masked_m=mm)
+    got = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=16)
+    want = ogemm.m_grouped_masked(qa, sa, qb, sb, masked_m)
+    for g, c in enumerate(mm):
+        assert np.all(got[g, c:] == SENTINEL), f"group {g}: rows beyond masked_m written"
+        if c:
+            assert_gemm_close(got[g, :c], want[g, :c], f"decode group {g}")
+    assert np.array_equal(got, _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=256))
 
 
 @pytest.mark.parametrize("idx", [0, 1])

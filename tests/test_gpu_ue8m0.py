@@ -133,12 +133,14 @@ def test_masked_packed_equals_fp32_path():
     pairs = [quant.per_block_cast(w.b[i], True) for i in range(g)]
     qb, sb = np.stack([p[0] for p in pairs]), np.stack([p[1] for p in pairs])
     out = []
-    for sa_t, sb_t in ((upload(sa), upload(sb)), (_pack(sa), _pack(sb))):
+    # expected_m 100 runs 256-row tiles, 16 the 64-row decode tiles: same bits
+    for sa_t, sb_t, hint in ((upload(sa), upload(sb), 100), (_pack(sa), _pack(sb), 100), (_pack(sa), _pack(sb), 16)):
         d = sentinel_like((g, max_m, n))
-        dg.m_grouped_fp8_gemm_nt_masked((upload_codes(qa), sa_t), (upload_codes(qb), sb_t), d, upload(masked_m), 100)
+        dg.m_grouped_fp8_gemm_nt_masked((upload_codes(qa), sa_t), (upload_codes(qb), sb_t), d, upload(masked_m), hint)
         torch.cuda.synchronize()
         out.append(bits(d))
     assert np.array_equal(out[0], out[1])
+    assert np.array_equal(out[1], out[2])
     want = ogemm.m_grouped_masked(qa, sa, qb, sb, masked_m)
     for i, c in enumerate(masked_m):
         assert np.all(out[1][i, c:] == SENTINEL)

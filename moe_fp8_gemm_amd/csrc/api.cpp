@@ -64,14 +64,14 @@ double instance_cost(GemmInstance inst, int64_t m_rows, int64_t groups_m_tiles_h
   const int64_t tiles = (groups_m_tiles_hint > 0 ? groups_m_tiles_hint : ceil_div(m_rows, info.bm)) *
                         ceil_div(n, info.bn);
   const int64_t rounds = ceil_div(tiles, cus);
-  const double factor = inst == kInstHuge ? 1.0 : (inst == kInstLarge ? 1.2 : 1.5);
+  const double factor = inst == kInstHuge ? 1.0 : inst == kInstTall ? 1.13 : inst == kInstLarge ? 1.2 : 1.5;
   return (double)rounds * info.bm * info.bn * factor;
 }
 
 GemmInstance choose_dense(int64_t m, int64_t n, int cus) {
   GemmInstance best = kInstMid;
   double best_cost = instance_cost(kInstMid, m, 0, n, cus);
-  for (GemmInstance inst : {kInstLarge, kInstHuge}) {
+  for (GemmInstance inst : {kInstLarge, kInstHuge, kInstTall}) {
     const double c = instance_cost(inst, m, 0, n, cus);
     if (c < best_cost) { best = inst; best_cost = c; }
   }

@@ -51,6 +51,7 @@ enum GemmInstance : int {
   kInstSkinny128 = 3, // 128 x 64 output tiles, 8 waves, 4-stage LDS pipeline (small M, usually split over K)
   kInstSkinny64 = 4,  // 64 x 64 output tiles, 8 waves, 4-stage LDS pipeline (M <= 64, usually split over K)
   kInstDecode = 5,    // 64 x 256 output tiles, 8 waves side by side, 3-stage LDS pipeline (masked, few rows)
+  kInstTall = 6,      // 192 x 256 output tiles, 8 waves, 2-stage LDS pipeline (dense, fills the device where 256x256 does not)
   kNumInstances
 };
 

@@ -849,6 +849,9 @@ using CfgLarge = Cfg<128, 256, 2, 4, 3>;
 using CfgMid = Cfg<128, 128, 2, 4, 3>;
 // Masked decode (few rows per group): one 64-row wave band across 256 columns.
 using CfgDecode = Cfg<64, 256, 1, 8, 3>;
+// Three quarters of the 256x256 tile (48-row wave bands): more tiles where the
+// 256x256 grid leaves CUs idle (N = 2112: 198 tiles instead of 144 at M = 4096).
+using CfgTall = Cfg<192, 256, 4, 2, 2>;
 
 // Variants compiled per configuration: bit v of Mask set = variant v available.
 template <class C, int Mask>
@@ -893,6 +896,7 @@ InstanceInfo instance_info(GemmInstance inst) {
     case kInstLarge: return {CfgLarge::BM, CfgLarge::BN, CfgLarge::kOcc};
     case kInstMid: return {CfgMid::BM, CfgMid::BN, CfgMid::kOcc};
     case kInstDecode: return {CfgDecode::BM, CfgDecode::BN, CfgDecode::kOcc};
+    case kInstTall: return {CfgTall::BM, CfgTall::BN, CfgTall::kOcc};
     default: return {0, 0};
   }
 }
@@ -905,6 +909,7 @@ hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int gr
     case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);
     case kInstMid: return launch_cfg<CfgMid, kAll>(v, p, grid, stream);
     case kInstDecode: return launch_cfg<CfgDecode, (1 << kMasked)>(v, p, grid, stream);
+    case kInstTall: return launch_cfg<CfgTall, (1 << kDense)>(v, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

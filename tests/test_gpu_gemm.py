@@ -130,11 +130,12 @@ def test_deterministic_and_independent_of_grid_width(m, n, k):
 
 
 # Several tiles per workgroup: 256x256 tiles (two LDS stages) with ragged M and
-# N edges and a last M tile whose waves are mostly idle, 128x256 tiles (three
-# stages) with three and with two K blocks (fewer blocks than stages).  A
-# narrow grid makes one or five workgroups walk all tiles in turn; the result
-# must not change.
-CHAINED = [(2600, 3104, 640, 256), (4100, 2056, 256, 256), (3000, 2504, 384, 128), (2048, 4096, 256, 128)]
+# N edges; 192x256 tiles (48-row wave bands) with ragged edges and with a last M
+# tile whose waves are mostly idle; 128x256 tiles (three stages) with three and
+# with two K blocks (fewer blocks than stages).  A narrow grid makes one or five
+# workgroups walk all tiles in turn; the result must not change.
+CHAINED = [(3800, 4088, 640, 256), (2600, 3104, 640, 192), (4100, 2056, 256, 192), (3000, 2504, 384, 128),
+           (2048, 4096, 256, 128)]
 
 
 @pytest.mark.parametrize("m,n,k,bm", CHAINED)

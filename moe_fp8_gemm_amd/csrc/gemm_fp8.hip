@@ -66,7 +66,8 @@ __device__ __forceinline__ int swz16(int row) { return (row & 7) ^ ((row >> 3) &
 // pass does not track them (it merges DMA histories conservatively at loop
 // headers and would wait for every DMA before each LDS read); the kernel waits
 // for them explicitly with s_waitcnt vmcnt.  No register is written by these
-// instructions: the data goes to LDS at M0 + 16 * lane (resp. 4 * lane).
+// instructions: the data goes to LDS at M0 + 16 * lane (resp. 4 * lane).  M0
+// is an input operand of the asm, so the compiler sets it and knows its value.
 __device__ __forceinline__ uint32_t lds_addr(const DG_LAS void* p) {
   return (uint32_t)(uintptr_t)p;
 }
@@ -79,12 +80,12 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(uniform_ptr(sbase)), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 __device__ __forceinline__ void dma4(const float* vaddr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(vaddr) : "memory", "m0");
+  asm volatile("global_load_lds_dword %0, off"
+               :: "v"(vaddr), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
 // Workgroup barrier that orders LDS accesses only (lgkmcnt), leaving DMA and

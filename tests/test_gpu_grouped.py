@@ -230,6 +230,46 @@ def test_masked_full_size_config3(idx):
                           f"config3[{idx}] group {gg}")
 
 
+@pytest.mark.parametrize("idx", [0, 1])
+def test_masked_decode_full_size(idx):
+    # The decode launch that the benchmark times: G=16 groups of up to 256 rows,
+    # at most 32 of them valid, and an expected_m hint of 16 (64-row tiles).  The
+    # same call with a hint of 128 (256-row tiles) must give the same bits.
+    n, k = synth.GROUPED_NK[idx]
+    g, max_m = 16, 256
+    seed = synth.seed_for(3, idx)
+    masked_m = synth.masked_counts(g, 32, seed + 500)
+    print(f"masked decode G=16 max_m=256 rows<=32 {n}x{k}", flush=True)
+    dev = device()
+    a32 = synth.draw_activation_device(g * max_m, k, seed, dev)
+    qa, sa = dg.per_token_cast_fp8(a32)
+    qb = torch.empty((g, n, k), dtype=torch.float8_e4m3fn, device=dev)
+    sb = torch.empty((g, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
+    for gg in range(g):
+        dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, gg, dev), q=qb[gg], sf=sb[gg])
+    a = (qa.view(g, max_m, k), sa.view(g, max_m, k // 128))
+    d = sentinel_like((g, max_m, n))
+    d_big = sentinel_like((g, max_m, n))
+    mm = upload(masked_m)
+    dg.m_grouped_fp8_gemm_nt_masked(a, (qb, sb), d, mm, 16)
+    dg.m_grouped_fp8_gemm_nt_masked(a, (qb, sb), d_big, mm, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), d_big.view(torch.int16)), "the hint changed the result"
+    rng = np.random.default_rng(seed + 1)
+    for gg in range(g):
+        c = int(masked_m[gg])
+        dv = d[gg].view(torch.int16)
+        assert bool((dv[c:] == SENTINEL).all()), f"group {gg}: rows beyond masked_m written"
+        assert bool(torch.isfinite(d[gg, :c].float()).all())
+        if c and gg % 4 == 1:
+            rows = sample_rows(rng, c, 6)
+            blocks, cols = sample_blocks_and_cols(rng, n, 2, 8)
+            b32 = synth.draw_weight_device(n, k, seed, gg, dev)
+            check_sampled(a32[gg * max_m:(gg + 1) * max_m], qa[gg * max_m:(gg + 1) * max_m],
+                          sa[gg * max_m:(gg + 1) * max_m], b32, qb[gg], sb[gg], d[gg], rows, blocks, cols,
+                          f"decode[{idx}] group {gg}")
+
+
 def test_masked_graph_capture_replays_with_new_counts():
     qa, sa, qb, sb, masked_m = _masked_host(6, 256, 392, 512, seed=23, masked_m=[10, 256, 0, 100, 129, 7])
     a = (upload_codes(qa), upload(sa))

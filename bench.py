@@ -16,11 +16,14 @@ The JSON line also carries:
   consecutive launches of that instance (event time / launches).  Events
   between launches cost GPU time, so the timed steps carry no others;
 * ``per_shape``: ``us_in_step`` from separate untimed steps with an event pair
-  around every launch, and cold-cache times (operands evicted before each run);
+  around every launch, and cold-cache times (operands evicted before each run).
+  Each shape also gets its roofline ceiling, min(FP8 peak, FLOPs / minimal
+  bytes x HBM peak), and the cold rate as a percentage of that ceiling (the
+  M <= 128 shapes are bound by streaming B, not by the MFMA);
 * ``cpu_baseline``: the CPU oracle timed on the full 4096x4096x7168 GEMM (4 runs);
-* ``extras``: cold-cache per-shape times, the MoE workloads (contiguous G=8,
-  masked G=16, Zipf contiguous G=256 with power-of-two scales) and the per-token
-  cast of a bf16 [32768, 7168] activation in GB/s.
+* ``extras``: the MoE workloads (contiguous G=8, masked G=16 with its decode
+  variant, Zipf contiguous G=256 with power-of-two scales), each with the same
+  ceiling, and the per-token cast of a bf16 [32768, 7168] activation in GB/s.
 """
 from __future__ import annotations
 
@@ -40,6 +43,19 @@ import synth  # noqa: E402
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def min_bytes(rows, n, k, groups=1):
+    """Bytes a GEMM must move at least: the useful A rows, every group's B, both
+    scale arrays and D, each once (fp32 scale words)."""
+    kb = k // 128
+    return rows * k + groups * n * k + 4 * rows * kb + 4 * groups * ((n + 127) // 128) * kb + 2 * rows * n
+
+
+def ceiling_tflops(flops, nbytes):
+    """Roofline ceiling of one GEMM: the smaller of the FP8 MFMA peak and its
+    arithmetic intensity times the HBM peak."""
+    return min(FP8_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3)
 
 
 def log(msg):
@@ -126,9 +142,11 @@ def bench_extras(dg, dev, reps):
         mi = torch.from_numpy(m_indices).to(dev)
         ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi), reps, flush)
         useful = 2.0 * int(counts.sum()) * n * k
+        ceil = ceiling_tflops(useful, min_bytes(int(counts.sum()), n, k, 8))
         out[f"contiguous_G8_{n}x{k}"] = {
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
-            "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "m_total": m_total}
+            "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "m_total": m_total,
+            "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil}
         del qa, sa, qb, sb, d
 
         masked_m = synth.config3_masked_m(idx)
@@ -148,9 +166,10 @@ def bench_extras(dg, dev, reps):
         ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm, 128), reps, flush)
         useful = 2.0 * int(masked_m.sum()) * n * k
         b_bytes = 16 * n * k
+        ceil = ceiling_tflops(useful, min_bytes(int(masked_m.sum()), n, k, 16))
         out[f"masked_G16_{n}x{k}"] = {
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS,
-            "b_read_gbs": b_bytes / ms / 1e6}
+            "b_read_gbs": b_bytes / ms / 1e6, "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil}
         # decode shape on the same operands: 0..32 rows per group, run on the
         # 64-row decode tiles (hint 16) and on the 256-row tiles (hint 128)
         mm_dec = torch.from_numpy(synth.masked_counts(16, 32, seed + 500)).to(dev)
@@ -205,7 +224,9 @@ def bench_extras(dg, dev, reps):
     ms_p = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, pa), (qb, pb), d, mi), max(3, reps // 2),
                          flush)
     useful = 2.0 * int(counts.sum()) * n * k
+    ceil = ceiling_tflops(useful, min_bytes(int(counts.sum()), n, k, 256))
     out["contiguous_zipf_G256_4096x7168_ue8m0"] = {
+        "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil,
         "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
         "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "b_read_gbs": 256 * n * k / ms / 1e6,
         "m_total": m_total, "us_packed_ue8m0_scales": ms_p * 1e3,
@@ -398,6 +419,9 @@ def main():
         per_shape[i]["us_cold"] = ms * 1e3
         per_shape[i]["tflops_cold"] = flops[i] / (ms * 1e-3) / 1e12
         per_shape[i]["pct_fp8_peak_cold"] = 100 * per_shape[i]["tflops_cold"] / FP8_PEAK_TFLOPS
+        ceil = ceiling_tflops(flops[i], min_bytes(*shapes[i]))
+        per_shape[i]["ceiling_tflops"] = ceil
+        per_shape[i]["pct_of_ceiling_cold"] = 100 * per_shape[i]["tflops_cold"] / ceil
     del flush
     result = {
         "metric": "FP8 block-scaled GEMM TFLOPS (1 GPU) and % of MI355X FP8 MFMA peak",

@@ -74,6 +74,16 @@ def test_dense_validation(lib):
     assert _gemm(lib, a=ctypes.c_void_p(0x10008)) == 2   # misaligned A
     assert _gemm(lib, m=0) == 0                          # empty problem: success, no launch
     assert _gemm(lib, n=0) == 0
+    assert _gemm(lib, m=0, k=0) == 0                     # empty before any other check
+    assert _gemm(lib, k=0, lda=0, ldb=0) == 2            # empty sum over K: not supported
+
+
+def test_dense_rejects_row_offsets_beyond_32_bits(lib):
+    # The kernels address operand rows with 32-bit byte offsets from the operand
+    # base: rows * ld must stay below 2^32 (these calls fail before any launch).
+    k = 65536
+    assert _gemm(lib, m=65536, k=k, lda=k, ldb=k, sfa_sm=k // 128, sfb_sn=k // 128) == 2
+    assert _gemm(lib, n=65536, ldd=65536, k=k, lda=k, ldb=k, sfa_sm=k // 128, sfb_sn=k // 128) == 2
 
 
 def test_workspace_entry_validation_and_size(lib):
@@ -103,8 +113,9 @@ def test_contiguous_validation(lib):
     f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
     i = ctypes.c_int64
 
-    def call(m_total=256, groups=2, m_idx=P, n=256, k=512):
-        return f(P, i(512), P, i(4), i(1), P, i(512), i(256 * 512), P, i(4), i(1), i(8), P, i(256),
+    def call(m_total=256, groups=2, m_idx=P, n=256, k=512, ld=512):
+        kb = ld // 128
+        return f(P, i(ld), P, i(kb), i(1), P, i(ld), i(256 * ld), P, i(kb), i(1), i(2 * kb), P, i(256),
                  m_idx, i(m_total), i(n), i(k), ctypes.c_int(groups), None)
 
     assert call(m_total=200) == 3                        # MISALIGNED_LAYOUT
@@ -112,6 +123,7 @@ def test_contiguous_validation(lib):
     assert call(m_idx=None) == 1
     assert call(k=500) == 2
     assert call(m_total=0) == 0
+    assert call(m_total=65536, k=65536, ld=65536) == 2   # A row offsets beyond 32 bits
 
 
 def test_masked_validation(lib):

@@ -106,7 +106,14 @@ class Flusher:
         torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def event_time_ms(fn, reps, flush=None):
+def event_time_ms(fn, reps, flush=None, warmup=5):
+    """Median HIP-event time of fn over reps runs, each after the cache flush.
+    The untimed warm-up runs (same flush) let the clocks settle first: the
+    first launches of a workload in a process run up to 10% slower."""
+    for _ in range(warmup):
+        if flush:
+            flush()
+        fn()
     times = []
     for _ in range(reps):
         if flush:

@@ -59,13 +59,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Static instance choice: estimated time = rounds of persistent tiles x tile
 // area x a per-instance cost factor (relative cycles per output element,
 // measured on MI355X: bigger tiles move fewer bytes through L2 and LDS per FLOP).
+double area_factor(GemmInstance inst) {
+  return inst == kInstHuge ? 1.0 : inst == kInstTall ? 1.13 : inst == kInstLarge ? 1.2 : 1.5;
+}
+
 double instance_cost(GemmInstance inst, int64_t m_rows, int64_t groups_m_tiles_hint, int64_t n, int cus) {
   const InstanceInfo info = instance_info(inst);
   const int64_t tiles = (groups_m_tiles_hint > 0 ? groups_m_tiles_hint : ceil_div(m_rows, info.bm)) *
                         ceil_div(n, info.bn);
   const int64_t rounds = ceil_div(tiles, cus);
-  const double factor = inst == kInstHuge ? 1.0 : inst == kInstTall ? 1.13 : inst == kInstLarge ? 1.2 : 1.5;
-  return (double)rounds * info.bm * info.bn * factor;
+  return (double)rounds * info.bm * info.bn * area_factor(inst);
 }
 
 GemmInstance choose_dense(int64_t m, int64_t n, int cus) {
@@ -172,6 +175,37 @@ int64_t plan_workspace_bytes(const DensePlan& pl) {
 GemmInstance choose_contiguous(int64_t m_total, int64_t n, int cus) {
   return instance_cost(kInstLarge, m_total, 0, n, cus) <= instance_cost(kInstMid, m_total, 0, n, cus)
              ? kInstLarge : kInstMid;
+}
+
+// Contiguous plan.  When the tiles of the chosen instance end in a thinly
+// filled last round, the M tiles of the whole rounds run in one launch and the
+// rows left over in a second launch of 128x128 tiles, which spreads them over
+// twice as many CUs.  A row's result does not depend on its tile, so the split
+// changes no bits.
+struct ContigPlan {
+  GemmInstance head, tail;
+  int64_t head_rows;   // rows of the first launch (m_total: one launch)
+};
+
+ContigPlan plan_contiguous(int64_t m_total, int64_t n, int cus) {
+  const GemmInstance inst = choose_contiguous(m_total, n, cus);
+  ContigPlan pl{inst, inst, m_total};
+  const InstanceInfo hi = instance_info(inst);
+  const int64_t tiles_n = ceil_div(n, hi.bn);
+  const int64_t slots = (int64_t)cus * hi.occ;
+  const int64_t tiles = (m_total / hi.bm) * tiles_n;
+  const int64_t head_rows = (tiles / slots) * slots / tiles_n * hi.bm;
+  if (inst == kInstMid || head_rows <= 0 || head_rows >= m_total) return pl;
+  const double round = (double)hi.bm * hi.bn * area_factor(inst);
+  const double whole = instance_cost(inst, m_total, 0, n, cus);
+  // a fifth of a round for the second launch's start and ramp
+  const double split = instance_cost(inst, head_rows, 0, n, cus) + instance_cost(kInstMid, m_total - head_rows, 0, n, cus) +
+                       0.2 * round;
+  if (split < whole) {
+    pl.tail = kInstMid;
+    pl.head_rows = head_rows;
+  }
+  return pl;
 }
 
 dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile_bound, hipStream_t stream) {
@@ -326,10 +360,23 @@ dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_
   p.m_indices = m_indices;
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
   p.sf_packed = packed ? 1 : 0;
-  const GemmInstance inst = choose_contiguous(m_total, n, device_cus());
-  const InstanceInfo info = instance_info(inst);
-  const int64_t tiles = (m_total / info.bm) * ceil_div(n, info.bn);
-  return launch(inst, kContiguous, p, tiles, static_cast<hipStream_t>(stream));
+  const ContigPlan pl = plan_contiguous(m_total, n, device_cus());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const InstanceInfo hi = instance_info(pl.head);
+  GemmParams ph = p;
+  ph.m = pl.head_rows;
+  st = launch(pl.head, kContiguous, ph, (pl.head_rows / hi.bm) * ceil_div(n, hi.bn), s);
+  if (st != DG_SUCCESS || pl.head_rows == m_total) return st;
+  // The rest of the rows: the same problem seen from row head_rows on.
+  const int64_t r0 = pl.head_rows;
+  const InstanceInfo ti = instance_info(pl.tail);
+  GemmParams pt = p;
+  pt.a += r0 * lda;
+  pt.sfa += r0 * sfa_sm;
+  pt.d += r0 * ldd;
+  pt.m_indices += r0;
+  pt.m = m_total - r0;
+  return launch(pl.tail, kContiguous, pt, (pt.m / ti.bm) * ceil_div(n, ti.bn), s);
 }
 
 }  // namespace

@@ -73,6 +73,37 @@ def test_contiguous_equals_dense_on_each_group_and_groups_are_independent():
     assert np.array_equal(got2[same], got[same])
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_contiguous_ragged_last_round_split(ue8m0):
+    # 12 M tiles x 4 N tiles of 128x256 = 48 tiles.  On a 20-CU grid the two
+    # whole rounds (10 M tiles) run in one launch and the last 2 M tiles in a
+    # second launch of 128x128 tiles; on 7 CUs it stays one launch.  Every grid
+    # must give the bits of the full-width grid, and those match the oracle.
+    w, qa, sa, qb, sb = _contig_host(4, 1100, 1024, 512, seed=5, ue8m0=ue8m0)
+    assert w.m_indices.size == 1536
+    a = (upload_codes(qa), upload(sa))
+    b = (upload_codes(qb), upload(sb))
+    if ue8m0:
+        a = (a[0], dg.pack_ue8m0(a[1]))
+        b = (b[0], dg.pack_ue8m0(b[1]))
+    mi = upload(w.m_indices)
+    pad = w.m_indices < 0
+    results = {}
+    for cus in (0, 20, 7):
+        dg.set_num_cus(cus)
+        try:
+            d = sentinel_like((qa.shape[0], qb.shape[1]))
+            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi)
+            torch.cuda.synchronize()
+        finally:
+            dg.set_num_cus(0)
+        results[cus] = bits(d)
+        assert np.all(results[cus][pad] == SENTINEL), f"{cus} CUs: padding rows were written"
+    assert np.array_equal(results[20], results[0]) and np.array_equal(results[7], results[0])
+    want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, w.m_indices)
+    assert_gemm_close(results[0][~pad], want[~pad], "contiguous, split launch")
+
+
 def test_contiguous_padding_block_skipped_and_hand_layout():
     # hand-made layout: a fully padded block, a 1-row group, a full block, ragged groups
     k, n, g = 256, 200, 4

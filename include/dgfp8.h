@@ -159,6 +159,9 @@ dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, size_t ws_
  * every row with m_indices >= 0 has the same value, which lies in
  * [0, num_groups).  The group of a block is read from its first row; a block
  * whose first row is -1 is skipped entirely.
+ * The work is one kernel launch, or two on the same stream when the tiles end
+ * in a thinly filled last round (the rows of the whole rounds first, then the
+ * remaining rows on narrower tiles); the results do not depend on the split.
  * Errors: m_total % 128 != 0 -> DG_ERROR_MISALIGNED_LAYOUT.
  * Page juejin.cn, sections 3 and 4(3) (M-only grouping, contiguous layout
  * aligned to the M block); page "GitHub 推荐…", 风险与不足 (128-row padding).

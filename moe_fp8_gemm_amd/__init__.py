@@ -312,3 +312,11 @@ def set_num_cus(num_cus: int) -> None:
 def get_num_cus() -> int:
     return lib.dg_get_num_cus()
 
+
+# The pages' names for the persistent-grid width (page ssnai.com DeepGEMM
+# analysis, 配置与调优建议: run-time tuning with set_num_sms).  On MI355X the unit
+# is the compute unit; the tensor-core-utilisation and programmatic-launch knobs
+# named beside it have no counterpart here.
+set_num_sms = set_num_cus
+get_num_sms = get_num_cus
+

@@ -191,3 +191,14 @@ def test_accumulate_entry_validation(lib):
     assert call(ldc=258) == 2                                  # ldc % 4
     assert call(c=ctypes.c_void_p(0x10008)) == 2               # c not 16-byte aligned
     assert call(c=None, m=0) == 0                              # empty problem
+
+
+def test_grid_width_setting_and_the_pages_names():
+    import moe_fp8_gemm_amd as dg
+    try:
+        dg.set_num_sms(7)
+        assert dg.get_num_cus() == 7 and dg.get_num_sms() == 7
+        dg.set_num_cus(0)                                    # back to every compute unit
+        assert dg.get_num_sms() == dg.get_num_cus() > 7
+    finally:
+        dg.set_num_cus(0)

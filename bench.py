@@ -11,7 +11,8 @@ whole-step TFLOPS (2*M*N*K summed over the step / wall time of K steps).
 The JSON line also carries:
 * ``roofline``: the dominant kernel (the tile/split instance that takes most of
   the step), algorithmic FLOPs per launch / its average launch time, against
-  the 5.0 PFLOP/s dense FP8 MFMA peak.  The launch time is measured inside the
+  the 5.0 PFLOP/s dense FP8 MFMA peak (2.4 GHz), and against 256 CUs x 8192
+  FLOP/clock at the clock the committed counter pass measured for it.  The launch time is measured inside the
   timed steps with HIP events on the launch stream, one pair around each run of
   consecutive launches of that instance (event time / launches).  Events
   between launches cost GPU time, so the timed steps carry no others;
@@ -281,11 +282,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.txt")
 GEMM_SOURCE = os.path.join(ROOT, "moe_fp8_gemm_amd", "csrc", "gemm_fp8.hip")
 
 
-def measured_traffic(cfg, shapes):
-    """HBM bytes per launch of the dominant instance, from the committed PMC
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a 1 GiB copy), or None
-    when there is none for this instance and shape set or the kernel source has
-    changed since the counters were taken."""
+def measured_profile(cfg, shapes):
+    """Counter figures of the dominant instance from the committed PMC summary:
+    HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a 1 GiB
+    copy) and the shader clock it ran at (GRBM_GUI_ACTIVE).  None when there is
+    none for this instance and shape set or the kernel source has changed since
+    the counters were taken."""
     import hashlib
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -299,7 +301,7 @@ def measured_traffic(cfg, shapes):
     if (kv.get("kernel_source_sha256") != sha or kv.get("tile") != "%dx%dx%d" % cfg
             or kv.get("shapes") != want_shapes):
         return None
-    return int(float(kv["hbm_bytes_per_launch"]))
+    return kv
 
 
 def main():
@@ -430,6 +432,11 @@ def main():
         per_shape[i]["ceiling_tflops"] = ceil
         per_shape[i]["pct_of_ceiling_cold"] = 100 * per_shape[i]["tflops_cold"] / ceil
     del flush
+    prof = measured_profile(dom_cfg, [shapes[i] for i in big])
+    # The 5.0 PFLOP/s peak assumes 2.4 GHz (256 CUs x 8192 FP8 FLOP per clock);
+    # the committed counter pass also gives the clock the kernel actually ran at.
+    sclk = float(prof["sclk_ghz"]) if prof and "sclk_ghz" in prof else None
+    peak_at_sclk = 256 * 8192 * sclk / 1e3 if sclk else None
     result = {
         "metric": "FP8 block-scaled GEMM TFLOPS (1 GPU) and % of MI355X FP8 MFMA peak",
         "value": round(value, 2),
@@ -449,11 +456,14 @@ def main():
                    "gemms_per_step": len(shapes), "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(dom_cfg, [shapes[i] for i in big]),
+                     "traffic": int(float(prof["hbm_bytes_per_launch"])) if prof else None,
                      "kernel": "dense %dx%d-tile GEMM%s" % (dom_cfg[0], dom_cfg[1],
                                                             "" if dom_cfg[2] == 1 else ", split-K %d" % dom_cfg[2]),
                      "shapes": ["%dx%dx%d" % shapes[i] for i in big],
-                     "avg_launch_us": round(dom_time * 1e3, 2), "flops_per_launch": dom_flops},
+                     "avg_launch_us": round(dom_time * 1e3, 2), "flops_per_launch": dom_flops,
+                     "sclk_ghz_profiled": sclk,
+                     "peak_at_profiled_sclk": round(peak_at_sclk, 1) if sclk else None,
+                     "frac_at_profiled_sclk": round(achieved / peak_at_sclk, 4) if sclk else None},
         "per_shape": per_shape,
     }
     if not args.no_extras:

@@ -104,6 +104,47 @@ def test_contiguous_ragged_last_round_split(ue8m0):
     assert_gemm_close(results[0][~pad], want[~pad], "contiguous, split launch")
 
 
+def test_contiguous_two_launch_plan_graph_replays_with_new_routing():
+    # The contiguous call on a 20-CU grid is two launches (see the ragged-round
+    # test above).  Captured once, the graph is replayed with the groups of the
+    # 128-row segments relabelled each time; every replay must match an eager
+    # call on the same grid bit for bit, and the oracle.
+    w, qa, sa, qb, sb = _contig_host(4, 1100, 1024, 512, seed=5)
+    a = (upload_codes(qa), upload(sa))
+    b = (upload_codes(qb), upload(sb))
+    mi = upload(w.m_indices)
+    d = sentinel_like((qa.shape[0], qb.shape[1]))
+    dg.set_num_cus(20)
+    try:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi)      # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi)
+        rng = np.random.default_rng(9)
+        for rep in range(3):
+            perm = rng.permutation(4).astype(np.int32)
+            new_idx = np.where(w.m_indices >= 0, perm[np.maximum(w.m_indices, 0)], -1).astype(np.int32)
+            mi.copy_(torch.from_numpy(new_idx))
+            d.view(torch.int16).fill_(SENTINEL)                    # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got = bits(d)
+            eager = _gpu_contig(qa, sa, qb, sb, new_idx)
+            assert np.array_equal(got, eager), rep
+            pad = new_idx < 0
+            assert np.all(got[pad] == SENTINEL)
+            want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, new_idx)
+            assert_gemm_close(got[~pad], want[~pad], f"replay {rep}")
+    finally:
+        dg.set_num_cus(0)
+
+
 def test_contiguous_padding_block_skipped_and_hand_layout():
     # hand-made layout: a fully padded block, a 1-row group, a full block, ragged groups
     k, n, g = 256, 200, 4

@@ -17,6 +17,11 @@ Modules:
 * ``ue8m0`` -- packing of exponent-only scales, four per int32 word.
 
 Every function is pinned by CPU tests against closed forms, library decoders,
-brute force and invariants; no function is "parity unpinned".
+brute force, exact-rational golden cases and invariants; no function is
+"parity unpinned".  tests/test_oracle_mutations.py plants one plausible mistake
+at a time in these functions (reciprocal instead of division in the scale or
+the quotient, a skipped fp32 rounding, ties away from zero, UE8M0 rounded down,
+no amax floor, bf16 truncation or double rounding, K-block scale order, the B
+scale index, a spurious factor, a dropped K block) and checks that a pin fails.
 """
 from . import bf16, e4m3, exact, gemm, quant, ue8m0  # noqa: F401

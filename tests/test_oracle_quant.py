@@ -1,5 +1,6 @@
-"""Pins of the oracle quantizers: hand-worked golden examples, closed forms,
-the partial last weight block, and the error bound of the encoding."""
+"""Pins of the oracle quantizers: hand-worked golden examples, exact-rational
+division cases, closed forms, the partial last weight block, and the error
+bound of the encoding."""
 import os
 
 import numpy as np
@@ -29,6 +30,38 @@ def test_golden_quant_examples():
         assert q[0, :len(expect)].tolist() == expect, name
         n += 1
     assert n == 6
+
+
+def _division_cases():
+    """Cases of tests/golden/quant_division_cases.txt (written in exact rational
+    arithmetic by make_quant_division_cases.py): values and scale as fp32 bits."""
+    for line in open(os.path.join(GOLDEN, "quant_division_cases.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            name, ue, xs, scale, codes = [f.strip() for f in line.split("|")]
+            vals = np.array([int(v, 16) for v in xs.split()], np.uint32).view(np.float32)
+            yield name, bool(int(ue)), vals, np.uint32(int(scale, 16)), [int(c, 16) for c in codes.split()]
+
+
+def test_division_cases_bit_exact():
+    """The scale is the correctly rounded fp32 amax/448 and each code comes from
+    the correctly rounded fp32 quotient x/s; a reciprocal multiply (amax*RN(1/448)
+    or x*RN(1/s)) or a quotient rounded straight to E4M3 fails these cases."""
+    n = 0
+    for name, ue, vals, scale_bits, want in _division_cases():
+        x = np.zeros((1, 128), np.float32)
+        x[0, :vals.size] = vals
+        q, s = quant.per_token_cast(x, ue8m0=ue)
+        assert s.view(np.uint32)[0, 0] == scale_bits, name
+        assert q[0, :vals.size].tolist() == want, name
+        # the same block as the first row of a 128x128 weight block
+        w = np.zeros((128, 128), np.float32)
+        w[0] = x[0]
+        qw, sw = quant.per_block_cast(w, ue8m0=ue)
+        assert sw.view(np.uint32)[0, 0] == scale_bits, name
+        assert qw[0, :vals.size].tolist() == want, name
+        n += 1
+    assert n == 20
 
 
 def test_scale_closed_forms():

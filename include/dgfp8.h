@@ -32,6 +32,12 @@
  *       sfb[nb * sfb_sn + kb * sfb_sk]; output column j uses nb = j / 128.
  *   E4M3 is the OCP "FN" flavour (largest finite 448, no infinities).
  *   Strides are in elements and must be >= 0.
+ *   Scale values: any finite fp32 (negative ones flip the sign of their block's
+ *   contribution).  A zero scale makes its block contribute nothing, as the
+ *   definition says; a subnormal scale (magnitude below 2^-126) is flushed to
+ *   zero, i.e. also contributes nothing.  An infinite or NaN scale gives NaN in
+ *   every output it weights (a row for an A scale, a 128-column block for a B
+ *   scale).  The casts never produce a scale below fp32(1e-4)/448.
  *
  * Alignment contract: K % 128 == 0; lda, ldb and the A/B base addresses are
  * multiples of 16 bytes; N % 8 == 0, ldd % 8 == 0 and D is 16-byte aligned.
@@ -55,7 +61,10 @@ typedef enum dg_status {
   DG_ERROR_LAUNCH = 4             /* HIP reported an error at launch */
 } dg_status;
 
-/* Human-readable name of a status; never NULL. */
+/* Human-readable name of a status; never NULL.  Errors are returned rather
+ * than raised, so the caller decides how to report them (page "GitHub 推荐：
+ * DeepSeek 开源周最大黑马 DeepGEMM…", 解法哲学 and 可复用的模式与技巧: host-side
+ * assertions on every layout field give the caller a clear error). */
 const char* dg_status_string(dg_status status);
 
 /*
@@ -135,10 +144,15 @@ dg_status dg_fp8_gemm_nt_acc(const void* a, int64_t lda,
 size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /* The output tile (block_m x block_n) and K split count dg_fp8_gemm_nt_ws
- * would use for this problem with a workspace of ws_bytes (0: none).  For
- * profiling and logs; the choice never changes results beyond the split-K
- * note above.  Errors: null outputs or non-positive sizes ->
- * DG_ERROR_INVALID_VALUE, k % 128 != 0 -> DG_ERROR_NOT_SUPPORTED. */
+ * would use for this problem with a workspace of ws_bytes (0: none).  The
+ * choice is a pure function of the shape and the device's compute-unit count,
+ * made by a cost model rather than by timing candidates (page "GitHub 推荐：
+ * DeepSeek 开源周最大黑马 DeepGEMM…", 创新之处 on the analytical heuristics
+ * that rank a small, constrained set of block shapes; page "企业官网建设流程
+ * 全解析", section 2.1 on per-shape configurations).  For profiling and logs; the
+ * choice never changes results beyond the split-K note above.  Errors: null
+ * outputs or non-positive sizes -> DG_ERROR_INVALID_VALUE, k % 128 != 0 ->
+ * DG_ERROR_NOT_SUPPORTED. */
 dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, size_t ws_bytes,
                                      int* block_m, int* block_n, int* splits);
 
@@ -231,6 +245,10 @@ dg_status dg_per_token_cast_fp8_f32(const void* x, int64_t ldx,
 /*
  * Weight-side cast: fp32 [n, k] -> E4M3 [n, k] with one scale per 128x128 block
  * (rows beyond n in the last block do not exist and do not enter its amax).
+ * The weights' block granularity is the method's (page "GitHub 推荐：DeepSeek
+ * 开源周最大黑马 DeepGEMM…", 问题判断); the pages tell users to prepare
+ * weights and scales with the library's weight conversion tools (page
+ * ssnai.com DeepGEMM analysis, the FP8/FP4 pitfall notes and Mega MoE steps).
  * Same scale and code rules as dg_per_token_cast_fp8, amax taken over the block.
  *   sf  device, fp32 [ceil(n/128), k/128]: element (nb, kb) at sf[nb * sf_sn + kb * sf_sk]
  */

@@ -113,6 +113,30 @@ def _packed(sa: torch.Tensor, sb: torch.Tensor) -> bool:
     return sa.dtype == torch.int32
 
 
+def _scale_words(k: int, packed: bool) -> int:
+    """Scale entries per row along K: one per 128-wide K block (fp32), or one
+    int32 word per 4 K blocks (packed UE8M0)."""
+    kb = k // 128
+    return (kb + 3) // 4 if packed else kb
+
+
+def _check_scale_shapes(sa: torch.Tensor, sb: torch.Tensor, lead: tuple, rows_a: int, n: int, k: int,
+                        packed: bool) -> None:
+    """The kernels index the scale arrays from (rows, n, k) alone, so a scale
+    tensor of the wrong shape would be read out of bounds: reject it here.
+    lead: leading (group) dimensions of both scale tensors."""
+    if k % 128:
+        return                       # the library rejects K % 128 != 0 itself
+    kw = _scale_words(k, packed)
+    want_a = tuple(lead) + (rows_a, kw)
+    want_b = tuple(lead) + ((n + 127) // 128, kw)
+    what = "packed UE8M0 int32" if packed else "float32"
+    if tuple(sa.shape) != want_a:
+        raise ValueError(f"sfa ({what}) must have shape {want_a}, got {tuple(sa.shape)}")
+    if tuple(sb.shape) != want_b:
+        raise ValueError(f"sfb ({what}) must have shape {want_b}, got {tuple(sb.shape)}")
+
+
 def _out_bf16(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype != torch.bfloat16 or not t.is_cuda or t.stride(-1) != 1:
         raise TypeError(f"{name} must be a bfloat16 device tensor with unit column stride")
@@ -120,7 +144,7 @@ def _out_bf16(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 _AUTO = "auto"
-_workspaces = {}
+_workspaces = {}      # (device index, stream handle) -> zero-initialised workspace
 
 
 def workspace_size(m: int, n: int, k: int) -> int:
@@ -138,14 +162,17 @@ def tile_config(m: int, n: int, k: int, workspace: bool = True) -> Tuple[int, in
 
 
 def _auto_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    # One zero-filled workspace per device, grown on demand.  Calls leave its
-    # counter block zero, so it is reused by every later call; calls that may run
-    # concurrently on different streams must pass their own workspaces.
+    # One zero-filled workspace per (device, stream), grown on demand.  Calls
+    # leave its counter block zero, so every later call on that stream reuses
+    # it; calls on different streams, which may overlap, never share one.  It is
+    # allocated (and zero-filled) on the stream that uses it, so the caching
+    # allocator hands its memory to no other stream while that one may use it.
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(idx)
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+    ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _workspaces[idx] = ws
+        _workspaces[key] = ws
     return ws
 
 
@@ -155,16 +182,21 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
 
     a = (codes [m, k], sfa [m, k/128]); b = (codes [n, k], sfb [ceil(n/128), k/128]);
     d bf16 [m, n] is overwritten and returned; c, when given, is an fp32 [m, n]
-    addend (fp32 scales only).  ``workspace``: "auto" (a cached per-device buffer,
-    enabling split-K for small m), None (never split), or a zero-initialised uint8
-    device tensor of at least ``workspace_size(m, n, k)`` bytes.
+    addend (fp32 scales only).  Packed UE8M0 scales (both int32) are
+    [m, ceil(k/512)] and [ceil(n/128), ceil(k/512)].  ``workspace``: "auto" (a
+    cached buffer per device and stream, enabling split-K for small m), None
+    (never split), or a zero-initialised uint8 device tensor of at least
+    ``workspace_size(m, n, k)`` bytes (calls that may overlap need distinct ones).
     """
     (qa, sa), (qb, sb) = a, b
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
+    if qa.dim() != 2 or qb.dim() != 2 or d.dim() != 2:
+        raise ValueError("a, b and d must be 2-D")
     m, k = qa.shape
     n = qb.shape[0]
     if qb.shape[1] != k or d.shape != (m, n):
         raise ValueError("shape mismatch")
+    _check_scale_shapes(sa, sb, (), m, n, k, _packed(sa, sb))
     if isinstance(workspace, str):
         if workspace != _AUTO:
             raise ValueError("workspace must be 'auto', None or a tensor")
@@ -202,10 +234,17 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
     if m_indices.dtype != torch.int32 or not m_indices.is_cuda:
         raise TypeError("m_indices must be an int32 device tensor")
+    if qa.dim() != 2 or qb.dim() != 3 or d.dim() != 2:
+        raise ValueError("a must be [m_total, k], b [G, n, k] and d [m_total, n]")
     m_total, k = qa.shape
     g, n, _ = qb.shape
     if qb.shape[2] != k or d.shape != (m_total, n) or m_indices.shape != (m_total,) or m_indices.stride(0) != 1:
         raise ValueError("shape mismatch")
+    if sa.dim() != 2 or sb.dim() != 3:
+        raise ValueError("sfa must be [m_total, k-words] and sfb [G, ceil(n/128), k-words]")
+    _check_scale_shapes(sa, sb[0], (), m_total, n, k, _packed(sa, sb))
+    if sb.shape[0] != g:
+        raise ValueError(f"sfb has {sb.shape[0]} groups, b has {g}")
     fn = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if _packed(sa, sb) else lib.dg_m_grouped_fp8_gemm_nt_contiguous
     _check(fn(
         qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
@@ -225,10 +264,13 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor,
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
     if masked_m.dtype != torch.int32 or not masked_m.is_cuda:
         raise TypeError("masked_m must be an int32 device tensor")
+    if qa.dim() != 3 or qb.dim() != 3 or d.dim() != 3:
+        raise ValueError("a must be [G, max_m, k], b [G, n, k] and d [G, max_m, n]")
     g, max_m, k = qa.shape
     n = qb.shape[1]
-    if qb.shape != (g, n, k) or d.shape != (g, max_m, n) or masked_m.shape != (g,):
+    if qb.shape != (g, n, k) or d.shape != (g, max_m, n) or masked_m.shape != (g,) or masked_m.stride(0) != 1:
         raise ValueError("shape mismatch")
+    _check_scale_shapes(sa, sb, (g,), max_m, n, k, _packed(sa, sb))
     fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if _packed(sa, sb) else lib.dg_m_grouped_fp8_gemm_nt_masked
     _check(fn(
         qa.data_ptr(), qa.stride(1), qa.stride(0),

@@ -214,9 +214,11 @@ __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, 
 // product m = m_a * m_b: before a K block's MFMAs it is rescaled by
 // m_prev / m, and the epilogue multiplies by the last m.  The MFMA therefore
 // accumulates straight into acc, and no VALU instruction waits on an MFMA
-// result inside the K loop (with power-of-two scales every ratio is 1).  Zero
-// or denormal scales have a biased exponent of 0, i.e. a weight of 2^-127 on
-// that block; infinities and NaNs give NaN.
+// result inside the K loop (with power-of-two scales every ratio is 1).  A
+// zero or subnormal scale (biased exponent 0) makes its block contribute
+// nothing: the A fragments of the rows it weights are cleared (all of them for
+// a B scale), which is exact for zero and flushes a subnormal scale to zero.
+// Infinities and NaNs (biased exponent 255) give NaN.
 __device__ __forceinline__ int scale_exponent(float s) {
   return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
 }
@@ -284,12 +286,21 @@ __device__ __forceinline__ void scale_math(BlockRegs<C>& r, float (&mant)[C::MS]
   }
   r.eb = scale_exponent(sb);
   const float mb = scale_mantissa(sb);
+  bool any_zero = r.eb == 0;
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
     r.ea[ms] = scale_exponent(sa[ms]);
+    any_zero = any_zero || r.ea[ms] == 0;
     const float m = scale_mantissa(sa[ms]) * mb;
     r.ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
     mant[ms] = keep ? mant[ms] : m;
+  }
+  // Zero or subnormal scales: rare, so one wave-uniform test guards the
+  // clearing of the fragments (lane l's A fragment holds K values of row l%16).
+  if (__builtin_amdgcn_ballot_w64(any_zero) != 0) {
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms)
+      if (r.eb == 0 || r.ea[ms] == 0) r.af[ms] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
 

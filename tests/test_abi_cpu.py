@@ -202,3 +202,31 @@ def test_grid_width_setting_and_the_pages_names():
         assert dg.get_num_sms() == dg.get_num_cus() > 7
     finally:
         dg.set_num_cus(0)
+
+
+# ------------------------------------------------------------------ binding: scale shapes
+
+def test_binding_rejects_scale_tensors_of_the_wrong_shape():
+    """The kernels index scales from (rows, n, k) alone, so the binding checks
+    the scale tensors' shapes per format before any pointer reaches the library."""
+    import torch
+    import moe_fp8_gemm_amd as m
+    chk = m._check_scale_shapes
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)   # noqa: E731
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)     # noqa: E731
+    # dense 300 x 264 x 1664: 13 K blocks -> 4 packed words; ceil(264/128) = 3 B blocks
+    chk(f32(300, 13), f32(3, 13), (), 300, 264, 1664, False)
+    chk(i32(300, 4), i32(3, 4), (), 300, 264, 1664, True)
+    for sa, sb, packed in ((f32(300, 12), f32(3, 13), False),    # a missing K block
+                           (f32(300, 13), f32(2, 13), False),    # floor(n/128) B blocks
+                           (f32(299, 13), f32(3, 13), False),    # a missing row
+                           (i32(300, 13), i32(3, 13), True),     # one int32 per K block, not packed words
+                           (i32(300, 4), i32(3, 3), True)):
+        with pytest.raises(ValueError):
+            chk(sa, sb, (), 300, 264, 1664, packed)
+    # grouped (masked): the group dimension leads both scale tensors
+    chk(f32(5, 200, 5), f32(5, 3, 5), (5,), 200, 264, 640, False)
+    with pytest.raises(ValueError):
+        chk(f32(4, 200, 5), f32(5, 3, 5), (5,), 200, 264, 640, False)
+    with pytest.raises(ValueError):
+        chk(i32(5, 200, 5), i32(5, 3, 2), (5,), 200, 264, 640, True)

@@ -2,16 +2,20 @@
 
 Covers bf16 and fp32 per-token (1x128) casts with fp32 and power-of-two scales,
 the 128x128 weight cast with a partial last block, planted edge rows (all zero,
-signed zeros, tiny values, exact ties after division, +-448), and the full
-bf16 [32768, 7168] activation of the Zipf MoE workload (sampled rows plus the
-planted ones).
+signed zeros, tiny values, exact ties after division, +-448), the exact-rational
+division cases of tests/golden/quant_division_cases.txt, every fp32 value of
+magnitude <= 448 through the E4M3 conversion, and every row of the full bf16
+[32768, 7168] activation of the Zipf MoE workload.
 """
+import concurrent.futures
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import synth
-from oracle import quant
+from oracle import e4m3, quant
 from gpu_util import codes, device
 
 pytestmark = pytest.mark.gpu
@@ -131,17 +135,122 @@ def test_per_block_rounding_boundaries(ue8m0):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+def _oracle_cast_rows(x32_chunks, ue8m0):
+    """The oracle quantizer over row chunks, several chunks at a time (numpy
+    releases the interpreter lock inside its array operations)."""
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda c: quant.per_token_cast(c, ue8m0), x32_chunks))
+
+
 @pytest.mark.parametrize("ue8m0", [False, True])
-def test_per_token_full_size_activation_sampled(ue8m0):
+def test_per_token_full_size_activation_every_row(ue8m0):
     x = synth.config4_cast_input()                         # bf16 [32768, 7168]
     x[:6] = torch.from_numpy(_plant_edges(np.zeros((6, x.shape[1]), np.float32))).to(torch.bfloat16)
     xd = x.to(device())
     q, s = dg.per_token_cast_fp8(xd, ue8m0=ue8m0)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(44)
-    rows = np.array(sorted(set(rng.choice(x.shape[0], 2048, replace=False).tolist()) | set(range(6)) | {x.shape[0] - 1}))
-    x32 = x[torch.as_tensor(rows)].float().numpy()
-    oq, os_ = quant.per_token_cast(x32, ue8m0)
-    ri = torch.as_tensor(rows, device=device())
-    assert np.array_equal(codes(q[ri]), oq)
-    assert np.array_equal(s[ri].cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    gq, gs = codes(q), s.cpu().numpy()
+    step = 1024
+    chunks = [x[r:r + step].float().numpy() for r in range(0, x.shape[0], step)]
+    for i, (oq, os_) in enumerate(_oracle_cast_rows(chunks, ue8m0)):
+        r = i * step
+        assert np.array_equal(gq[r:r + step], oq), f"codes differ in rows {r}..{r + step - 1}"
+        assert np.array_equal(gs[r:r + step].view(np.uint32), os_.view(np.uint32)), f"scales, rows {r}.."
+    print(f"all {x.shape[0]} rows bit-exact (ue8m0={ue8m0})", flush=True)
+
+
+def _division_cases():
+    path = os.path.join(os.path.dirname(__file__), "golden", "quant_division_cases.txt")
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            name, ue, xs, scale, cs = [f.strip() for f in line.split("|")]
+            yield (name, bool(int(ue)), np.array([int(v, 16) for v in xs.split()], np.uint32).view(np.float32),
+                   int(scale, 16), [int(c, 16) for c in cs.split()])
+
+
+def test_division_cases_on_the_gpu_casts():
+    """Quotients within a few fp32 ulps of E4M3 midpoints and scales where
+    amax/448 and amax*RN(1/448) round apart: the GPU's divisions must be the
+    correctly rounded ones (expected values derived in exact rational arithmetic)."""
+    cases = list(_division_cases())
+    x = np.zeros((len(cases), 256), np.float32)
+    for i, (_, _, vals, _, _) in enumerate(cases):
+        x[i, :vals.size] = vals
+        x[i, 128:128 + vals.size] = -vals                # the same block negated
+    assert not any(ue for _, ue, _, _, _ in cases)
+    q, s = dg.per_token_cast_fp8(torch.from_numpy(x).to(device()))
+    w = np.zeros((128 * len(cases), 128), np.float32)
+    w[::128] = x[:, :128]
+    qw, sw = dg.per_block_cast_fp8(torch.from_numpy(w).to(device()))
+    torch.cuda.synchronize()
+    gq, gs, gqw, gsw = codes(q), s.cpu().numpy().view(np.uint32), codes(qw), sw.cpu().numpy().view(np.uint32)
+    for i, (name, _, vals, scale_bits, want) in enumerate(cases):
+        nv = vals.size
+        assert gs[i, 0] == scale_bits and gs[i, 1] == scale_bits, name
+        assert gq[i, :nv].tolist() == want, name
+        assert gq[i, 128:128 + nv].tolist() == [c ^ 0x80 for c in want], name
+        assert gsw[i, 0] == scale_bits and gqw[128 * i, :nv].tolist() == want, name
+
+
+def _e4m3_first_bits():
+    """For each non-negative code c, the first fp32 bit pattern the oracle
+    encoder maps to c (the encoder is monotone in the value; bisection)."""
+    top = int(np.float32(448.0).view(np.uint32))
+    enc = lambda b: int(e4m3.encode(np.array([b], np.uint32).view(np.float32).astype(np.float64))[0])  # noqa: E731
+    first = [0]
+    for c in range(1, 0x7F):
+        lo, hi = first[-1], top                            # enc(lo) < c <= enc(hi)
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if enc(mid) >= c:
+                hi = mid
+            else:
+                lo = mid
+        assert enc(hi) == c and enc(hi - 1) == c - 1
+        first.append(hi)
+    return np.array(first + [top + 1], np.int64)
+
+
+def test_e4m3_conversion_exhaustive():
+    """Every fp32 value of magnitude <= 448, both signs, through the fp32
+    per-token cast with a block amax of 448 (scale 1, quotient = the value), so
+    the codes are the hardware conversion's.  Along increasing bit patterns the
+    codes must never decrease and each code must occur exactly as often as the
+    oracle encoder's interval for it is long: together that is equality with
+    the oracle on every value."""
+    first = _e4m3_first_bits()
+    want_counts = np.diff(first)                           # values per code 0x00..0x7E
+    total = int(first[-1])                                 # bit patterns 0 .. 0x43E00000
+    dev = device()
+    per_row = 127                                          # column 0 holds the amax 448
+    rows = 1 << 20
+    for sign in (0, 1):
+        counts = torch.zeros(128, dtype=torch.int64, device=dev)
+        prev_last = torch.zeros((), dtype=torch.int64, device=dev)
+        for start in range(0, total, rows * per_row):
+            n_vals = min(rows * per_row, total - start)
+            r = -(-n_vals // per_row)
+            pat = torch.arange(start, start + r * per_row, dtype=torch.int64, device=dev)
+            pat = torch.clamp(pat, max=total - 1)
+            if sign:
+                pat = pat - (1 << 31)                      # the int32 whose bits are pattern | 0x80000000
+            x = torch.empty((r, 128), dtype=torch.float32, device=dev)
+            x[:, 0] = 448.0
+            x[:, 1:] = pat.to(torch.int32).view(torch.float32).view(r, per_row)
+            q, s = dg.per_token_cast_fp8(x)
+            assert bool((s == 1.0).all())
+            cq = q.view(torch.uint8)[:, 1:].reshape(-1)[:n_vals].to(torch.int64)
+            assert bool(((cq >> 7) == sign).all()), "sign bit"
+            mag = cq & 0x7F
+            assert bool((mag[1:] >= mag[:-1]).all()), f"codes decrease inside the chunk at {start}"
+            assert bool(mag[0] >= prev_last), f"codes decrease at the chunk start {start}"
+            prev_last = mag[-1]
+            counts += torch.bincount(mag, minlength=128)
+            del x, q, s, pat, cq, mag
+        got = counts.cpu().numpy()
+        assert got[0x7F] == 0
+        bad = np.nonzero(got[:0x7F] != want_counts)[0]
+        assert bad.size == 0, f"sign {sign}: code counts differ at {[hex(int(c)) for c in bad[:8]]}"
+        print(f"sign {sign}: {total} values, all codes match the oracle", flush=True)

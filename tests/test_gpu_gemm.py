@@ -226,6 +226,79 @@ def test_split_k_consecutive_problems_share_the_workspace():
         assert_gemm_close(bits(d), ogemm.gemm_nt(qa, sa, qb, sb), f"{qa.shape[0]}x{qb.shape[0]}")
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 520, 4096), (4096, 4096, 512)])
+def test_zero_subnormal_and_nonfinite_scales(m, n, k):
+    """A zero scale contributes nothing (the plain definition); a subnormal one
+    is flushed to zero; an infinite or NaN one gives NaN in the rows (or the
+    128-column block) it weights.  Covers the 128x128 / split-K / 256x256 tiles."""
+    print(f"special scales {m}x{n}x{k} tile {dg.tile_config(m, n, k)}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + n)
+    sub = np.float32(1e-40)                         # subnormal fp32
+    sa[5, :] = 0.0                                  # whole row: exactly zero output
+    sa[7, 2] = 0.0
+    sa[9, 1] = -0.0
+    sa[11, 3] = sub
+    sa[12, 0] = -sub
+    sb[1, 0] = 0.0                                  # B block of columns 128..255, K block 0
+    sb[0, 3] = sub
+    sa[13, 1] = np.inf                              # row 13: NaN
+    sb[2, 2] = np.nan                               # columns 256..383: NaN
+    got = _gpu_dense(qa, sa, qb, sb)
+    ftz = lambda x: np.where(np.abs(x) < np.float32(2.0 ** -126), np.float32(0), x).astype(np.float32)  # noqa: E731
+    sa_ref, sb_ref = ftz(sa), ftz(sb)
+    sa_ref[13, 1], sb_ref[2, 2] = 1.0, 1.0          # placeholders: those outputs are checked for NaN below
+    want = ogemm.gemm_nt(qa, sa_ref, qb, sb_ref)
+    f = (got.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(f[13])) and np.all(np.isnan(f[:, 256:384]))
+    keep_r = np.array([i for i in range(m) if i != 13])
+    keep_c = np.array([j for j in range(n) if not 256 <= j < 384])
+    assert np.all(f[5, keep_c] == 0.0), "a row whose scales are all zero must be exactly zero"
+    assert_gemm_close(got[np.ix_(keep_r, keep_c)], want[np.ix_(keep_r, keep_c)], f"special scales {m}x{n}x{k}")
+
+
+def test_split_k_auto_workspace_on_two_concurrent_streams():
+    """Split-K calls with the default workspace on two streams that overlap:
+    each stream gets its own workspace, so neither corrupts the other's partial
+    tiles or arrival counters."""
+    shapes = [(64, 2112, 7168), (128, 7168, 2048)]
+    for s in shapes:
+        assert dg.tile_config(*s)[2] > 1, "shape no longer splits"
+    probs = [_host_problem(m, n, k, seed=90 + i) for i, (m, n, k) in enumerate(shapes)]
+    dev_in = [((upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb))) for qa, sa, qb, sb in probs]
+    wants = [ogemm.gemm_nt(*p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(6):
+        for i, st in enumerate(streams):
+            j = (i + rep) % 2                               # both shapes on both streams
+            (m, n, _) = shapes[j]
+            with torch.cuda.stream(st):
+                d = sentinel_like((m, n))
+                dg.fp8_gemm_nt(dev_in[j][0], dev_in[j][1], d)
+                outs.append((j, d))
+    torch.cuda.synchronize()
+    first = {}
+    for j, d in outs:
+        got = bits(d)
+        if j not in first:
+            assert_gemm_close(got, wants[j], f"stream split-K {shapes[j]}")
+            first[j] = got
+        assert np.array_equal(got, first[j]), f"{shapes[j]}: a concurrent call changed the result"
+
+
+def test_binding_rejects_wrong_scale_shapes_before_launch():
+    qa, sa, qb, sb = _host_problem(128, 264, 512, seed=3)
+    a, b = upload_codes(qa), upload_codes(qb)
+    d = sentinel_like((128, 264))
+    with pytest.raises(ValueError):
+        dg.fp8_gemm_nt((a, upload(sa[:, :3])), (b, upload(sb)), d)
+    with pytest.raises(ValueError):
+        dg.fp8_gemm_nt((a, upload(sa)), (b, upload(sb[:2])), d)
+    torch.cuda.synchronize()
+    assert bool((d.view(torch.int16) == 0x7FC1).all()), "output touched"
+
+
 # ------------------------------------------------------------------ full size, sampled
 
 def sample_rows(rng, m, count):
@@ -271,6 +344,12 @@ def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=F
     return assert_gemm_close(got, want, what)
 
 
+def mn_major_scales(rows, kblocks):
+    """fp32 scale buffer [rows, kblocks] in the MN-major layout (element (r, kb)
+    at kb * rows + r) that the casts write and the benchmark's GEMMs read."""
+    return torch.empty((kblocks, rows), dtype=torch.float32, device=device()).t()
+
+
 @pytest.mark.parametrize("idx", range(15))
 def test_dense_full_size_sampled(idx):
     m, n, k = synth.config1_shapes()[idx]
@@ -279,7 +358,8 @@ def test_dense_full_size_sampled(idx):
     dev = device()
     a32 = synth.draw_activation_device(m, k, seed, dev)
     b32 = synth.draw_weight_device(n, k, seed, 0, dev)
-    qa, sa = dg.per_token_cast_fp8(a32)
+    qa, sa = dg.per_token_cast_fp8(a32, sf=mn_major_scales(m, k // 128))
+    assert sa.stride() == (1, m)
     qb, sb = dg.per_block_cast_fp8(b32)
     d = sentinel_like((m, n))
     dg.fp8_gemm_nt((qa, sa), (qb, sb), d)
@@ -290,3 +370,31 @@ def test_dense_full_size_sampled(idx):
     check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, f"{m}x{n}x{k}")
     # every output element was written (no sentinel left, nothing non-finite)
     assert bool(torch.isfinite(d.float()).all())
+
+
+def test_dense_full_size_every_element():
+    """4096 x 4096 x 7168 as the benchmark runs it (MN-major A scales from the
+    cast, 256x256 tiles): every output element against the oracle, which
+    re-quantizes the whole fp32 operands (its codes and scales must equal the
+    GPU casts' bit for bit)."""
+    m, n, k = 4096, 4096, 7168
+    idx = synth.config1_shapes().index((m, n, k))
+    seed = synth.seed_for(1, idx)
+    assert dg.tile_config(m, n, k) == (256, 256, 1)
+    dev = device()
+    a32 = synth.draw_activation_device(m, k, seed, dev)
+    b32 = synth.draw_weight_device(n, k, seed, 0, dev)
+    qa, sa = dg.per_token_cast_fp8(a32, sf=mn_major_scales(m, k // 128))
+    qb, sb = dg.per_block_cast_fp8(b32)
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt((qa, sa), (qb, sb), d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    oqa, osa = quant.per_token_cast(a32.cpu().numpy())
+    oqb, osb = quant.per_block_cast(b32.cpu().numpy())
+    assert np.array_equal(codes(qa), oqa) and np.array_equal(sa.cpu().numpy().view(np.uint32), osa.view(np.uint32))
+    assert np.array_equal(codes(qb), oqb) and np.array_equal(sb.cpu().numpy().view(np.uint32), osb.view(np.uint32))
+    print("oracle casts agree; computing the full reference", flush=True)
+    want = ogemm.gemm_nt(oqa, osa, oqb, osb)
+    stats = assert_gemm_close(got, want, f"{m}x{n}x{k} every element")
+    print(f"every element within tolerance, rel. Frobenius {stats['fro']:.2e}", flush=True)

@@ -161,14 +161,18 @@ def test_contiguous_padding_block_skipped_and_hand_layout():
     assert_gemm_close(got[~pad], want[~pad], "hand layout")
 
 
-def _contig_full(counts, m_indices, n, k, seed, ue8m0, what, rows_per_group_sample):
+def _contig_full(counts, m_indices, n, k, seed, ue8m0, what, rows_per_group_sample, packed=False):
+    """Full-size contiguous run as the benchmark does it: A scales written by the
+    cast in the MN-major layout; with ``packed`` both scale arrays are then
+    packed to UE8M0 words (A's words MN-major) and the packed GEMM runs."""
     dev = device()
     g = counts.size
     m_total = m_indices.size
     valid = torch.as_tensor(np.nonzero(m_indices >= 0)[0], device=dev)
     a32 = torch.zeros((m_total, k), dtype=torch.float32, device=dev)
     a32[valid] = synth.draw_activation_device(int(valid.numel()), k, seed, dev)
-    qa, sa = dg.per_token_cast_fp8(a32, ue8m0=ue8m0)
+    sa_mn = torch.empty((k // 128, m_total), dtype=torch.float32, device=dev).t()
+    qa, sa = dg.per_token_cast_fp8(a32, ue8m0=ue8m0, sf=sa_mn)
     qb = torch.empty((g, n, k), dtype=torch.float8_e4m3fn, device=dev)
     sb = torch.empty((g, (n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
     for gg in range(g):
@@ -177,7 +181,13 @@ def _contig_full(counts, m_indices, n, k, seed, ue8m0, what, rows_per_group_samp
         del w32
     d = sentinel_like((m_total, n))
     mi = upload(m_indices)
-    dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi)
+    if packed:
+        words = (k // 128 + 3) // 4
+        pa = dg.pack_ue8m0(sa, out=torch.empty((words, m_total), dtype=torch.int32, device=dev).t())
+        pb = dg.pack_ue8m0(sb)
+        dg.m_grouped_fp8_gemm_nt_contiguous((qa, pa), (qb, pb), d, mi)
+    else:
+        dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi)
     torch.cuda.synchronize()
     # padding rows untouched, every valid row written
     pad = torch.as_tensor(m_indices < 0, device=dev)
@@ -211,6 +221,13 @@ def test_contiguous_full_size_config4_pow2_scales():
     n, k = synth.CONFIG4_NK
     print(f"contiguous G=256 {m_indices.size}x{n}x{k}", flush=True)
     _contig_full(counts, m_indices, n, k, synth.seed_for(4, 0), True, "config4", 4)
+
+
+def test_contiguous_full_size_config4_packed_ue8m0():
+    counts, m_indices = synth.config4_routing()
+    n, k = synth.CONFIG4_NK
+    print(f"contiguous G=256 packed UE8M0 {m_indices.size}x{n}x{k}", flush=True)
+    _contig_full(counts, m_indices, n, k, synth.seed_for(4, 0), True, "config4 packed", 4, packed=True)
 
 
 # ------------------------------------------------------------------ masked

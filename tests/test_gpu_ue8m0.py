@@ -148,6 +148,21 @@ def test_masked_packed_equals_fp32_path():
             assert_gemm_close(out[1][i, :c], want[i, :c], f"masked packed group {i}")
 
 
+def test_dense_packed_256x256_tiles_mn_major_words():
+    """The instance the benchmark times with packed scales: 256x256 tiles, A
+    scale words in the MN-major layout.  Same bits as the fp32-scale path on the
+    same power-of-two scales, and every element against the oracle."""
+    m, n, k = 4096, 4096, 1536
+    assert dg.tile_config(m, n, k) == (256, 256, 1)
+    print(f"dense ue8m0 256x256 tiles {m}x{n}x{k}", flush=True)
+    qa, sa, qb, sb = _dense_pow2(m, n, k, seed=17)
+    words = ue8m0.pack(sa)
+    packed = _run_dense(qa, upload(np.ascontiguousarray(words.T)).t(), qb, _pack(sb))
+    fp32 = _run_dense(qa, upload(np.ascontiguousarray(sa.T)).t(), qb, upload(sb))
+    assert np.array_equal(packed, fp32)
+    assert_gemm_close(packed, ogemm.gemm_nt(qa, sa, qb, sb), f"packed 256x256 {m}x{n}x{k}")
+
+
 def test_mixed_scale_formats_rejected():
     qa, sa, qb, sb = _dense_pow2(128, 256, 512, seed=1)
     d = sentinel_like((128, 256))

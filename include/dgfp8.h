@@ -58,7 +58,8 @@ typedef enum dg_status {
   DG_ERROR_INVALID_VALUE = 1,     /* null pointer, negative size, bad stride, bad group count */
   DG_ERROR_NOT_SUPPORTED = 2,     /* K % 128 != 0, misaligned pointer / leading dimension, N % 8 != 0 */
   DG_ERROR_MISALIGNED_LAYOUT = 3, /* contiguous layout: m_total % 128 != 0 */
-  DG_ERROR_LAUNCH = 4             /* HIP reported an error at launch */
+  DG_ERROR_LAUNCH = 4,            /* HIP reported an error at launch */
+  DG_ERROR_SCRATCH_LIMIT = 5      /* dg_fp8_gemm_nt_noalloc: the problem needs more split-K scratch than its static maximum */
 } dg_status;
 
 /* Human-readable name of a status; never NULL.  Errors are returned rather
@@ -137,6 +138,32 @@ dg_status dg_fp8_gemm_nt_acc(const void* a, int64_t lda,
                              int64_t m, int64_t n, int64_t k,
                              void* ws, size_t ws_bytes,
                              void* stream);
+
+/*
+ * Dense GEMM for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments (without ws, ws_bytes) and results as dg_fp8_gemm_nt_ws given
+ * a workspace of dg_fp8_gemm_nt_workspace_size(m, n, k) bytes: the split-K
+ * partial tiles and arrival counters live in a static device array of the
+ * library instead, 16 MiB of partials plus the 256 KiB counter block
+ * (16.25 MiB per device, held from the device's first such call until the
+ * process ends).  Nothing is allocated and nothing is freed.
+ *   A problem whose split plan needs more than that returns
+ *   DG_ERROR_SCRATCH_LIMIT before anything is launched (call
+ *   dg_fp8_gemm_nt_ws with a workspace of your own instead).
+ *   Every call on one device shares that device's array: calls that may
+ *   overlap on one device (other streams, other host threads) race and give
+ *   wrong results; calls in order on one stream are safe.  The counters are
+ *   zero when the array is first used and every completed call leaves them
+ *   zero.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const void* a, int64_t lda,
+                                 const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                 const void* b, int64_t ldb,
+                                 const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                 void* d, int64_t ldd,
+                                 int64_t m, int64_t n, int64_t k,
+                                 void* stream);
 
 /* Workspace bytes dg_fp8_gemm_nt_ws needs to split this problem; 0 when the
  * problem runs unsplit (or the sizes are invalid).  Depends only on m, n, k

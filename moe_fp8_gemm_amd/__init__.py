@@ -62,6 +62,8 @@ _SIGNATURES = {
     "dg_pack_ue8m0": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p], _i32),
     "dg_fp8_gemm_nt_acc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
                             _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "dg_fp8_gemm_nt_noalloc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
+                                _i64, _i64, _i64, _p], _i32),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -73,6 +75,7 @@ DG_ERROR_INVALID_VALUE = 1
 DG_ERROR_NOT_SUPPORTED = 2
 DG_ERROR_MISALIGNED_LAYOUT = 3
 DG_ERROR_LAUNCH = 4
+DG_ERROR_SCRATCH_LIMIT = 5
 
 
 class DgError(RuntimeError):
@@ -223,6 +226,29 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
               qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
               d.data_ptr(), d.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream()),
            "dg_fp8_gemm_nt")
+    return d
+
+
+def fp8_gemm_nt_noalloc(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
+                        d: torch.Tensor) -> torch.Tensor:
+    """fp8_gemm_nt (fp32 scales) for callers that cannot allocate: split-K runs in
+    the library's static per-device scratch instead of a workspace.  Raises
+    DgError (DG_ERROR_SCRATCH_LIMIT) when the problem's split plan needs more
+    scratch than that holds.  Calls that may overlap on one device race."""
+    (qa, sa), (qb, sb) = a, b
+    _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
+    if qa.dim() != 2 or qb.dim() != 2 or d.dim() != 2:
+        raise ValueError("a, b and d must be 2-D")
+    m, k = qa.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k or d.shape != (m, n):
+        raise ValueError("shape mismatch")
+    if _packed(sa, sb):
+        raise NotImplementedError("the no-allocation GEMM takes fp32 scales")
+    _check_scale_shapes(sa, sb, (), m, n, k, False)
+    _check(lib.dg_fp8_gemm_nt_noalloc(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
+                                      qb.data_ptr(), qb.stride(0), sb.data_ptr(), sb.stride(0), sb.stride(1),
+                                      d.data_ptr(), d.stride(0), m, n, k, _stream()), "dg_fp8_gemm_nt_noalloc")
     return d
 
 

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdgfp8.so")
-SOURCES = ["api.cpp", "gemm_fp8.hip", "cast_fp8.hip"]
+SOURCES = ["api.cpp", "gemm_fp8.hip", "cast_fp8.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

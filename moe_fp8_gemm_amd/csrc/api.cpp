@@ -234,6 +234,7 @@ DG_EXPORT const char* dg_status_string(dg_status status) {
     case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED";
     case DG_ERROR_MISALIGNED_LAYOUT: return "DG_ERROR_MISALIGNED_LAYOUT";
     case DG_ERROR_LAUNCH: return "DG_ERROR_LAUNCH";
+    case DG_ERROR_SCRATCH_LIMIT: return "DG_ERROR_SCRATCH_LIMIT";
   }
   return "DG_ERROR_UNKNOWN";
 }

@@ -47,6 +47,7 @@ def test_status_strings_and_constants(lib):
     lib.dg_status_string.restype = ctypes.c_char_p
     assert lib.dg_status_string(0) == b"DG_SUCCESS"
     assert lib.dg_status_string(3) == b"DG_ERROR_MISALIGNED_LAYOUT"
+    assert lib.dg_status_string(5) == b"DG_ERROR_SCRATCH_LIMIT"
     assert lib.dg_get_mk_alignment_for_contiguous_layout() == 128
 
 

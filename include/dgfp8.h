@@ -32,12 +32,13 @@
  *       sfb[nb * sfb_sn + kb * sfb_sk]; output column j uses nb = j / 128.
  *   E4M3 is the OCP "FN" flavour (largest finite 448, no infinities).
  *   Strides are in elements and must be >= 0.
- *   Scale values: any finite fp32 (negative ones flip the sign of their block's
- *   contribution).  A zero scale makes its block contribute nothing, as the
- *   definition says; a subnormal scale (magnitude below 2^-126) is flushed to
- *   zero, i.e. also contributes nothing.  An infinite or NaN scale gives NaN in
- *   every output it weights (a row for an A scale, a 128-column block for a B
- *   scale).  The casts never produce a scale below fp32(1e-4)/448.
+ *   Scale values (fp32 entry points): finite fp32, negative ones flipping the
+ *   sign of their block's contribution.  A zero scale makes its block
+ *   contribute nothing, as the definition says.  Subnormal scales are applied
+ *   exactly as long as the product sfa * sfb of a row's block is at least
+ *   2^-189; smaller products contribute nothing.  A product of 2^65 or more,
+ *   or an infinite or NaN scale, gives NaN in every output it weights.  (The
+ *   casts produce scales between fp32(1e-4)/448 and 2^121.)
  *
  * Alignment contract: K % 128 == 0; lda, ldb and the A/B base addresses are
  * multiples of 16 bytes; N % 8 == 0, ldd % 8 == 0 and D is 16-byte aligned.

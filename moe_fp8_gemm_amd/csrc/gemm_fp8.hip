@@ -205,20 +205,26 @@ __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, 
   return (i32x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-// Scale application.  The product c = sa * sb of a row's A scale and the
-// wave's B scale is split as c = 2^e * m, m in [1, 4) carrying the signs.  The
-// block-scaled MFMA multiplies the K block's products by 2^e exactly: its E8M0
-// operands are the fp32 biased exponents of sb (B-row port, one per wave) and
-// of sa (A-row port, per lane: lane l supplies row l%16, the row its results
-// belong to).  The accumulator is kept in units of the current mantissa
-// product m = m_a * m_b: before a K block's MFMAs it is rescaled by
-// m_prev / m, and the epilogue multiplies by the last m.  The MFMA therefore
-// accumulates straight into acc, and no VALU instruction waits on an MFMA
-// result inside the K loop (with power-of-two scales every ratio is 1).  A
-// zero or subnormal scale (biased exponent 0) makes its block contribute
-// nothing: the A fragments of the rows it weights are cleared (all of them for
-// a B scale), which is exact for zero and flushes a subnormal scale to zero.
-// Infinities and NaNs (biased exponent 255) give NaN.
+// Scale application.  A row's scale product c = sa * sb for a K block is
+// applied as c = 2^e * m, m in [1, 2) carrying the sign.  The block-scaled
+// MFMA multiplies the K block's products by 2^e exactly through its E8M0
+// operands: the B-row port (one per wave) always gets 2^-63, and the A-row
+// port (per lane: lane l supplies row l%16, the row its results belong to)
+// gets the biased exponent of q = sa * (sb * 2^63) = c * 2^63, so that
+// 2^-63 * 2^(exponent of q) = 2^e.  The accumulator is kept in units of the
+// current mantissa m: before a K block's MFMAs it is rescaled by m_prev / m,
+// and the epilogue multiplies by the last m.  The MFMA therefore accumulates
+// straight into acc, and no VALU instruction waits on an MFMA result inside
+// the K loop (with power-of-two scales every ratio is 1).
+//   Special values come out of q on their own: a zero scale gives q = 0,
+// exponent 0, weight 2^-190, and the block's contribution (below 2^-165)
+// rounds away, so it adds exactly nothing, as the definition says.  A
+// subnormal scale is applied exactly as long as the product is at least
+// 2^-189 (q is then normal).  An infinite or NaN scale, or a product of 2^65
+// or more, makes q infinite or NaN, exponent 255, which the MFMA reads as
+// NaN.
+constexpr int kBRowScaleE8M0 = 127 - 63;   // 2^-63 on the B-row port (fp32-scale kernels)
+
 __device__ __forceinline__ int scale_exponent(float s) {
   return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
 }
@@ -284,23 +290,15 @@ __device__ __forceinline__ void scale_math(BlockRegs<C>& r, float (&mant)[C::MS]
     for (int ms = 0; ms < C::MS; ++ms) r.ea[ms] = (int)((__builtin_bit_cast(uint32_t, sa[ms]) >> sh) & 0xFFu);
     return;
   }
-  r.eb = scale_exponent(sb);
-  const float mb = scale_mantissa(sb);
-  bool any_zero = r.eb == 0;
+  r.eb = kBRowScaleE8M0;
+  const float sb63 = sb * 0x1p63f;   // exact unless sb >= 2^65 (then q is inf or NaN)
 #pragma unroll
   for (int ms = 0; ms < C::MS; ++ms) {
-    r.ea[ms] = scale_exponent(sa[ms]);
-    any_zero = any_zero || r.ea[ms] == 0;
-    const float m = scale_mantissa(sa[ms]) * mb;
+    const float q = sa[ms] * sb63;
+    r.ea[ms] = scale_exponent(q);
+    const float m = scale_mantissa(q);
     r.ratio[ms] = mant[ms] * __builtin_amdgcn_rcpf(m);
     mant[ms] = keep ? mant[ms] : m;
-  }
-  // Zero or subnormal scales: rare, so one wave-uniform test guards the
-  // clearing of the fragments (lane l's A fragment holds K values of row l%16).
-  if (__builtin_amdgcn_ballot_w64(any_zero) != 0) {
-#pragma unroll
-    for (int ms = 0; ms < C::MS; ++ms)
-      if (r.eb == 0 || r.ea[ms] == 0) r.af[ms] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
 

@@ -231,3 +231,29 @@ def test_binding_rejects_scale_tensors_of_the_wrong_shape():
         chk(f32(4, 200, 5), f32(5, 3, 5), (5,), 200, 264, 640, False)
     with pytest.raises(ValueError):
         chk(i32(5, 200, 5), i32(5, 3, 2), (5,), 200, 264, 640, True)
+
+
+# ------------------------------------------------------------------ build: resource report
+
+def test_build_resource_report_parser_and_no_scratch():
+    """The build parses the compiler's kernel-resource-usage remarks; the last
+    build's report (if present) shows no kernel with scratch memory or VGPR spills."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("dgfp8_build", os.path.join(ROOT, "moe_fp8_gemm_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    text = "\n".join([
+        "x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     TotalSGPRs: 104 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     VGPRs: 226 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 292 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     VGPRs Spill: 104 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     LDS Size [bytes/block]: 135168 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    k = b.parse_resource_remarks(text)
+    assert k == [{"name": "_Z1kv", "sgpr": 104, "vgpr": 226, "agpr": 0, "scratch": 292, "vspill": 104, "lds": 135168}]
+    report = os.path.join(ROOT, "moe_fp8_gemm_amd", "_build", "resource_usage.txt")
+    if os.path.exists(report):
+        rows = [l.split() for l in open(report).read().splitlines()[1:] if l.strip()]
+        assert rows and all(r[3] == "0" and r[4] == "0" for r in rows), "a kernel uses scratch or spills VGPRs"

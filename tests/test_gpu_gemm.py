@@ -228,24 +228,25 @@ def test_split_k_consecutive_problems_share_the_workspace():
 
 @pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 520, 4096), (4096, 4096, 512)])
 def test_zero_subnormal_and_nonfinite_scales(m, n, k):
-    """A zero scale contributes nothing (the plain definition); a subnormal one
-    is flushed to zero; an infinite or NaN one gives NaN in the rows (or the
-    128-column block) it weights.  Covers the 128x128 / split-K / 256x256 tiles."""
+    """A zero scale contributes nothing and a subnormal one its exact value (the
+    plain definition); an infinite or NaN scale gives NaN in the rows (or the
+    128-column block) it weights.  Covers the 128x64 / split-K / 256x256 tiles."""
     print(f"special scales {m}x{n}x{k} tile {dg.tile_config(m, n, k)}", flush=True)
     qa, sa, qb, sb = _host_problem(m, n, k, seed=m + n)
-    sub = np.float32(1e-40)                         # subnormal fp32
+    sub = np.float32(2.0 ** -130)                   # subnormal fp32
+    sb[:, 0] *= np.float32(2.0 ** 60)               # K block 0: products of sub with sb are normal
     sa[5, :] = 0.0                                  # whole row: exactly zero output
     sa[7, 2] = 0.0
     sa[9, 1] = -0.0
     sa[11, 3] = sub
+    sa[12, :] = 0.0                                 # row 12: only a subnormal-scaled block contributes
     sa[12, 0] = -sub
-    sb[1, 0] = 0.0                                  # B block of columns 128..255, K block 0
+    sb[1, 1] = 0.0                                  # B block of columns 128..255, K block 1
     sb[0, 3] = sub
     sa[13, 1] = np.inf                              # row 13: NaN
     sb[2, 2] = np.nan                               # columns 256..383: NaN
     got = _gpu_dense(qa, sa, qb, sb)
-    ftz = lambda x: np.where(np.abs(x) < np.float32(2.0 ** -126), np.float32(0), x).astype(np.float32)  # noqa: E731
-    sa_ref, sb_ref = ftz(sa), ftz(sb)
+    sa_ref, sb_ref = sa.copy(), sb.copy()
     sa_ref[13, 1], sb_ref[2, 2] = 1.0, 1.0          # placeholders: those outputs are checked for NaN below
     want = ogemm.gemm_nt(qa, sa_ref, qb, sb_ref)
     f = (got.astype(np.uint32) << 16).view(np.float32)
@@ -253,6 +254,8 @@ def test_zero_subnormal_and_nonfinite_scales(m, n, k):
     keep_r = np.array([i for i in range(m) if i != 13])
     keep_c = np.array([j for j in range(n) if not 256 <= j < 384])
     assert np.all(f[5, keep_c] == 0.0), "a row whose scales are all zero must be exactly zero"
+    assert np.any(f[12, keep_c] != 0.0)
+    assert_gemm_close(got[12, keep_c], want[12, keep_c], "row weighted by a subnormal scale only")
     assert_gemm_close(got[np.ix_(keep_r, keep_c)], want[np.ix_(keep_r, keep_c)], f"special scales {m}x{n}x{k}")
 
 

@@ -358,6 +358,18 @@ dg_status dg_pack_ue8m0(const float* sf, int64_t sf_s0, int64_t sf_s1,
                         int64_t rows, int64_t kblocks,
                         void* stream);
 
+/*
+ * Plan of the contiguous grouped GEMM: 0 (default) picks by the cost model;
+ * 1 forces the paired plan (256-row tiles on pairs of consecutive 128-row
+ * blocks of one group, found on the device from m_indices, and 128-row tiles on
+ * the blocks no pair covers: two launches); 2 forces one tile per 128-row
+ * block.  Layouts of more than 2048 blocks always take plan 2.  Every plan
+ * computes each output row with the same operations, so the choice never
+ * changes a bit of the result; it is a tuning and testing knob, process-wide.
+ * Errors: plan outside 0..2 -> DG_ERROR_INVALID_VALUE.
+ */
+dg_status dg_set_contiguous_plan(int plan);
+
 /* Row alignment of each group's segment in the contiguous layout: 128.
  * (Page ssnai.com DeepGEMM analysis: the alignment query for contiguous MoE.) */
 int dg_get_mk_alignment_for_contiguous_layout(void);

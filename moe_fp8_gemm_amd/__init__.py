@@ -62,6 +62,7 @@ _SIGNATURES = {
     "dg_pack_ue8m0": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p], _i32),
     "dg_fp8_gemm_nt_acc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
                             _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
+    "dg_set_contiguous_plan": ([_i32], _i32),
     "dg_fp8_gemm_nt_noalloc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
                                 _i64, _i64, _i64, _p], _i32),
 }
@@ -379,6 +380,12 @@ def set_num_cus(num_cus: int) -> None:
 
 def get_num_cus() -> int:
     return lib.dg_get_num_cus()
+
+
+def set_contiguous_plan(plan: int) -> None:
+    """Contiguous grouped GEMM plan: 0 cost model (default), 1 paired 256-row
+    tiles + leftover 128-row blocks, 2 one tile per 128-row block.  Same bits."""
+    _check(lib.dg_set_contiguous_plan(int(plan)), "dg_set_contiguous_plan")
 
 
 # The pages' names for the persistent-grid width (page ssnai.com DeepGEMM

@@ -4,6 +4,7 @@
 // choice of a compiled kernel instance, and launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -19,6 +20,7 @@ constexpr int kMaxMaskedGroups = 1024;
 constexpr int kMaxDevices = 64;
 
 int g_num_cus_override = 0;
+int g_contig_plan = 0;   // 0: cost model, 1: paired plan, 2: one tile per 128-row block
 int g_device_cus[kMaxDevices] = {0};
 
 // Compute units of the current device (ignores the override).
@@ -187,6 +189,9 @@ struct ContigPlan {
   int64_t head_rows;   // rows of the first launch (m_total: one launch)
 };
 
+// Estimated cost (same units as instance_cost) of a contiguous plan.
+double contig_plan_cost(const ContigPlan& pl, int64_t m_total, int64_t n, int cus);
+
 ContigPlan plan_contiguous(int64_t m_total, int64_t n, int cus) {
   const GemmInstance inst = choose_contiguous(m_total, n, cus);
   ContigPlan pl{inst, inst, m_total};
@@ -206,6 +211,27 @@ ContigPlan plan_contiguous(int64_t m_total, int64_t n, int cus) {
     pl.head_rows = head_rows;
   }
   return pl;
+}
+
+double contig_plan_cost(const ContigPlan& pl, int64_t m_total, int64_t n, int cus) {
+  if (pl.head_rows >= m_total) return instance_cost(pl.head, m_total, 0, n, cus);
+  return instance_cost(pl.head, pl.head_rows, 0, n, cus) + instance_cost(pl.tail, m_total - pl.head_rows, 0, n, cus) +
+         0.2 * instance_info(pl.head).bm * instance_info(pl.head).bn * area_factor(pl.head);
+}
+
+// Paired contiguous plan (see grouped_contiguous).  The host does not know the
+// routing, so the pair count is estimated: half of the groups end in a single
+// block.  Returns the instance for the single blocks and the estimated cost.
+GemmInstance paired_singles_instance(int64_t nblocks, int64_t n, int num_groups, int cus, double* cost) {
+  const double singles = (double)std::min<int64_t>(num_groups, nblocks) / 2.0;
+  const int64_t single_rows = (int64_t)(singles + 0.5) * 128;
+  const int64_t pair_rows = (nblocks * 128 - single_rows) / 256 * 256;
+  const GemmInstance si = instance_cost(kInstMid, single_rows, 0, n, cus) <=
+                                  instance_cost(kInstLarge, single_rows, 0, n, cus)
+                              ? kInstMid : kInstLarge;
+  *cost = instance_cost(kInstHuge, pair_rows, 0, n, cus) + instance_cost(si, single_rows, 0, n, cus) +
+          0.2 * instance_info(si).bm * instance_info(si).bn * area_factor(si);
+  return si;
 }
 
 dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile_bound, hipStream_t stream) {
@@ -361,8 +387,30 @@ dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_
   p.m_indices = m_indices;
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
   p.sf_packed = packed ? 1 : 0;
-  const ContigPlan pl = plan_contiguous(m_total, n, device_cus());
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // Paired plan: when the groups average at least two 128-row blocks, pairs of
+  // consecutive blocks of one group run as 256-row tiles (the largest, most
+  // efficient tile) and the blocks left over as 128-row tiles in a second
+  // launch.  Both launches find their tiles on the device from m_indices, so
+  // the plan needs no host read and stays graph-capturable.  Each row's result
+  // is computed the same way whatever its tile, so no bit changes.
+  const int64_t nblocks = m_total / kContiguousAlignment;
+  const ContigPlan pl = plan_contiguous(m_total, n, device_cus());
+  if (nblocks <= kMaxContigPairBlocks && g_contig_plan != 2) {
+    double paired_cost = 0.0;
+    const GemmInstance single = paired_singles_instance(nblocks, n, num_groups, device_cus(), &paired_cost);
+    // the model must predict a clear gain: within 10% the two plans measure alike
+    if (g_contig_plan == 1 || paired_cost < 0.9 * contig_plan_cost(pl, m_total, n, device_cus())) {
+      const InstanceInfo hi = instance_info(kInstHuge);
+      GemmParams pp = p;
+      pp.contig_mode = 1;
+      st = launch(kInstHuge, kContiguous, pp, (nblocks / 2) * ceil_div(n, hi.bn), s);
+      if (st != DG_SUCCESS) return st;
+      GemmParams ps = p;
+      ps.contig_mode = 2;
+      return launch(single, kContiguous, ps, nblocks * ceil_div(n, instance_info(single).bn), s);
+    }
+  }
   const InstanceInfo hi = instance_info(pl.head);
   GemmParams ph = p;
   ph.m = pl.head_rows;
@@ -537,4 +585,10 @@ DG_EXPORT dg_status dg_set_num_cus(int num_cus) {
 }
 
 DG_EXPORT int dg_get_num_cus(void) { return device_cus(); }
+
+DG_EXPORT dg_status dg_set_contiguous_plan(int plan) {
+  if (plan < 0 || plan > 2) return DG_ERROR_INVALID_VALUE;
+  g_contig_plan = plan;
+  return DG_SUCCESS;
+}
 

@@ -41,7 +41,14 @@ struct GemmParams {
   // scale format: 0 = fp32 scales, 1 = packed UE8M0 (int32 words holding the
   // exponents of 4 consecutive K blocks; sfa/sfb then point at those words)
   int sf_packed;
+  // contiguous only: 0 = a tile per BM-row block; 1 = 256-row tiles on pairs of
+  // consecutive blocks of one group; 2 = 128-row tiles on the blocks no pair
+  // covers (tile lists built on the device from m_indices)
+  int contig_mode;
 };
+
+// Largest number of 128-row blocks (m_total / 128) a paired contiguous plan takes.
+constexpr int kMaxContigPairBlocks = 2048;
 
 // Kernel instances the host can pick (see gemm_fp8.hip for the tile shapes).
 enum GemmInstance : int {

@@ -225,6 +225,11 @@ __device__ __forceinline__ i32x8 read_frag(DG_LAS uint8_t* base, uint32_t off0, 
 // NaN.
 constexpr int kBRowScaleE8M0 = 127 - 63;   // 2^-63 on the B-row port (fp32-scale kernels)
 
+// Raw buffer descriptors (word 3 of the resource: 32-bit data, no swizzle) and
+// the cache-policy operand of buffer accesses that are coherent device-wide.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kScopeDevice = 16;   // sc1
+
 __device__ __forceinline__ int scale_exponent(float s) {
   return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
 }
@@ -502,6 +507,69 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& mt,
   nt = in / gm;
 }
 
+// Contiguous layout, device-side tile list (one wave; graph-safe, the host never
+// reads m_indices).  A 128-row block belongs to the group m_indices holds at
+// its first row (-1: padding, no tile).  Consecutive blocks of one group form a
+// segment; from each segment's start, blocks are taken in pairs (a 256-row
+// tile) and an odd segment ends in a single block.  mode 1 lists the first
+// block of every pair, mode 2 every single block; the two launches of a plan
+// together cover every non-padding block exactly once.  Each lane walks 32
+// consecutive blocks; a max-scan over lanes hands each lane the start of the
+// segment its first block belongs to.
+constexpr int kMaxContigBlocks = kMaxContigPairBlocks;
+
+__device__ void contig_tile_list(const GemmParams& p, int lane, DG_LAS int16_t* list, DG_LAS int* count) {
+  constexpr int kPer = kMaxContigBlocks / 64;
+  const int nb = (int)(p.m / kKBlock);
+  const int b0 = lane * kPer;
+  auto group_of = [&](int b) -> int { return b >= 0 && b < nb ? p.m_indices[(int64_t)b * kKBlock] : -1; };
+  int g[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) g[i] = group_of(b0 + i);
+  const int gprev = group_of(b0 - 1), gnext = group_of(b0 + kPer);
+  int last = -1;   // last segment start in this lane's blocks
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int prev = i ? g[i - 1] : gprev;
+    if (g[i] >= 0 && g[i] != prev) last = b0 + i;
+  }
+  int incl = last;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl = max(incl, v);
+  }
+  int start = __shfl_up(incl, 1, 64);
+  if (lane == 0) start = -1;
+  uint32_t pick = 0;
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = b0 + i;
+    const int prev = i ? g[i - 1] : gprev;
+    if (g[i] < 0) continue;
+    if (g[i] != prev) start = b;
+    if (((b - start) & 1) == 0) {
+      const bool pair = (i + 1 < kPer ? g[i + 1] : gnext) == g[i];
+      if (pair == (p.contig_mode == 1)) {
+        pick |= 1u << i;
+        ++n;
+      }
+    }
+  }
+  int run = n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(run, off, 64);
+    if (lane >= off) run += v;
+  }
+  int pos = run - n;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if ((pick >> i) & 1u) list[pos++] = (int16_t)(b0 + i);
+  if (lane == 63) *count = run;
+}
+
 template <class C, int V>
 __global__ void __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kWaves * C::kOcc / 4, C::kWaves * C::kOcc / 4)))
@@ -557,6 +625,16 @@ gemm_kernel(GemmParams p) {
     tiles_m = (int)((p.m + C::BM - 1) / C::BM);
     num_tiles = tiles_m * tiles_n * (V == kDenseSplitK ? p.splits : 1);
   }
+  __shared__ int16_t contig_list[V == kContiguous ? kMaxContigBlocks : 1];
+  __shared__ int contig_count;
+  if constexpr (V == kContiguous) {
+    if (p.contig_mode != 0) {
+      if (wave == 0) contig_tile_list(p, lane, (DG_LAS int16_t*)contig_list, (DG_LAS int*)&contig_count);
+      __syncthreads();
+      tiles_m = contig_count;
+      num_tiles = tiles_m * tiles_n;
+    }
+  }
 
   // Tile state: position, group, K blocks and DMA sources.  okmask bit ms:
   // this lane's row of sub-tile ms is written.  The epilogue's global loads
@@ -565,6 +643,7 @@ gemm_kernel(GemmParams p) {
   // a load placed after them would wait for them too.
   struct Tile {
     int mt, nt, g, split, kbs;
+    int m0;                 // first row of the tile (per group when masked)
     uint32_t okmask;
     TileSrc<C> src;
   };
@@ -592,12 +671,13 @@ gemm_kernel(GemmParams p) {
         raster(tile / p.splits, tiles_m, tiles_n, mt, nt);
       } else {
         raster(tile, tiles_m, tiles_n, mt, nt);
-        if constexpr (V == kContiguous) {
-          g = p.m_indices[(int64_t)mt * C::BM];
-          if (g < 0) return false;              // whole block is padding
-        }
       }
-      const int64_t m0 = (int64_t)mt * C::BM;
+      int64_t m0 = (int64_t)mt * C::BM;
+      if constexpr (V == kContiguous) {
+        if (p.contig_mode != 0) m0 = (int64_t)contig_list[mt] * kKBlock;   // listed block
+        g = p.m_indices[m0];
+        if (g < 0) return false;                // whole block is padding
+      }
       const int64_t n0 = (int64_t)nt * C::BN;
       const int64_t a_rows = p.m;   // rows of A present in memory (per group when masked)
 
@@ -670,6 +750,7 @@ gemm_kernel(GemmParams p) {
     t.a_base = uniform_ptr(t.a_base);
     t.b_base = uniform_ptr(t.b_base);
     s.mt = __builtin_amdgcn_readfirstlane(mt);
+    s.m0 = __builtin_amdgcn_readfirstlane((int)m0);
     s.nt = __builtin_amdgcn_readfirstlane(nt);
     s.g = __builtin_amdgcn_readfirstlane(g);
     s.split = __builtin_amdgcn_readfirstlane(split);
@@ -698,7 +779,7 @@ gemm_kernel(GemmParams p) {
   auto store_tile = [&](const Tile& s, f32x4 (&acc)[C::MS][C::NS]) {
     uint16_t* D = p.d + (V == kMasked ? (int64_t)s.g * p.d_gs : 0);
     const int er16 = lane & 15, eq = lane >> 4;
-    const int64_t m0 = (int64_t)s.mt * C::BM, n0 = (int64_t)s.nt * C::BN;
+    const int64_t m0 = s.m0, n0 = (int64_t)s.nt * C::BN;
 #pragma unroll
     for (int ms = 0; ms < C::MS; ++ms) {
       if (!((s.okmask >> ms) & 1u)) continue;
@@ -772,24 +853,26 @@ gemm_kernel(GemmParams p) {
       // Publish this unit's partial tile, count arrivals; the last unit of the
       // output tile adds all partials in split order (deterministic whatever the
       // arrival order) and writes D.  Partials are kept in register order, not
-      // as a matrix: element c of acc[ms][j] of lane l of wave w sits at
-      // ((w * MS * NS + ms * NS + j) * 4 + c) * 64 + l, so that every store and
-      // load instruction covers 256 contiguous bytes.  The units of one tile may
-      // run on different XCDs, whose L2 caches are not coherent with each other
-      // for plain accesses: the partials move by device-scope relaxed atomic
-      // stores and loads (written through to / read from the device-coherent
-      // level), which avoids the L2-wide writeback and invalidate that a
-      // device-scope fence costs.
+      // as a matrix: the 4 floats of acc[ms][j] of lane l of wave w sit at float
+      // ((w * MS * NS + ms * NS + j) * 64 + l) * 4 of the split's region, so that
+      // each 16-byte store or load instruction covers 1 KB contiguous.  The
+      // units of one tile may run on different XCDs, whose L2 caches are not
+      // coherent with each other for plain accesses: the partials move with
+      // device-scope (sc1) buffer accesses, written through to and read from the
+      // device-coherent level, which avoids the L2-wide writeback and invalidate
+      // that a device-scope fence costs.  The buffer's size bounds every access.
       const int tile_mn = cur.mt * tiles_n + cur.nt;
-      float* part = p.ws + (int64_t)tile_mn * p.splits * (C::BM * C::BN) + wave * (C::kMfmas * 256) + lane;
+      constexpr int kTileFloats = C::BM * C::BN;
+      const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+          p.ws + (int64_t)tile_mn * p.splits * kTileFloats, 0, p.splits * kTileFloats * 4, kRawBufferFlags);
+      const int lane_off = ((wave * C::kMfmas) * 64 + lane) * 16;   // bytes, (ms, j) = (0, 0)
 #pragma unroll
       for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
         for (int j = 0; j < C::NS; ++j)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            __hip_atomic_store(part + (int64_t)cur.split * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
-                               acc[ms][j][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[ms][j]), part,
+                                                 lane_off + (ms * C::NS + j) * 1024,
+                                                 cur.split * kTileFloats * 4, kScopeDevice);
       // every partial store has been acknowledged before the arrival is counted
       __builtin_amdgcn_s_waitcnt(WaitVmLgkm0<0>::value);
       __shared__ int last_flag;
@@ -803,21 +886,30 @@ gemm_kernel(GemmParams p) {
         for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
           for (int j = 0; j < C::NS; ++j) acc[ms][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < p.splits; ++sp) {
-          // all of a split's loads first, then the adds: one wait, not one per load
-          f32x4 v[C::MS][C::NS];
+        // Splits in batches: every load of a batch is issued before the first
+        // add, so one memory round trip serves the whole batch; the adds then
+        // run in split order.
+        constexpr int kBatch = 32 / (C::kMfmas * 4) > 0 ? 32 / (C::kMfmas * 4) : 1;
+        for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
+          f32x4 v[kBatch][C::MS][C::NS];
 #pragma unroll
-          for (int ms = 0; ms < C::MS; ++ms)
+          for (int b = 0; b < kBatch; ++b)
 #pragma unroll
-            for (int j = 0; j < C::NS; ++j)
+            for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-              for (int c = 0; c < 4; ++c)
-                v[ms][j][c] = __hip_atomic_load(part + (int64_t)sp * (C::BM * C::BN) + ((ms * C::NS + j) * 4 + c) * 64,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int j = 0; j < C::NS; ++j)
+                v[b][ms][j] = sp0 + b < p.splits
+                                  ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  part, lane_off + (ms * C::NS + j) * 1024,
+                                                                  (sp0 + b) * kTileFloats * 4, kScopeDevice))
+                                  : (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ms = 0; ms < C::MS; ++ms)
+          for (int b = 0; b < kBatch; ++b)
 #pragma unroll
-            for (int j = 0; j < C::NS; ++j) acc[ms][j] += v[ms][j];
+            for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+              for (int j = 0; j < C::NS; ++j)
+                if (sp0 + b < p.splits) acc[ms][j] += v[b][ms][j];
         }
         // ready for the next call
         if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -913,7 +1005,7 @@ InstanceInfo instance_info(GemmInstance inst) {
 
 hipError_t launch_gemm(GemmInstance inst, Variant v, const GemmParams& p, int grid, hipStream_t stream) {
   switch (inst) {
-    case kInstHuge: return launch_cfg<CfgHuge, (1 << kDense) | (1 << kMasked)>(v, p, grid, stream);
+    case kInstHuge: return launch_cfg<CfgHuge, (1 << kDense) | (1 << kMasked) | (1 << kContiguous)>(v, p, grid, stream);
     case kInstSkinny128: return launch_cfg<CfgSkinny128, kDenseAndSplit>(v, p, grid, stream);
     case kInstSkinny64: return launch_cfg<CfgSkinny64, kDenseAndSplit>(v, p, grid, stream);
     case kInstLarge: return launch_cfg<CfgLarge, kAll>(v, p, grid, stream);

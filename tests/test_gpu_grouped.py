@@ -73,12 +73,26 @@ def test_contiguous_equals_dense_on_each_group_and_groups_are_independent():
     assert np.array_equal(got2[same], got[same])
 
 
+class _contig_plan:
+    """Force a contiguous plan (1 paired, 2 one tile per block) inside a with-block."""
+
+    def __init__(self, plan):
+        self.plan = plan
+
+    def __enter__(self):
+        dg.set_contiguous_plan(self.plan)
+
+    def __exit__(self, *exc):
+        dg.set_contiguous_plan(0)
+
+
 @pytest.mark.parametrize("ue8m0", [False, True])
 def test_contiguous_ragged_last_round_split(ue8m0):
-    # 12 M tiles x 4 N tiles of 128x256 = 48 tiles.  On a 20-CU grid the two
-    # whole rounds (10 M tiles) run in one launch and the last 2 M tiles in a
-    # second launch of 128x128 tiles; on 7 CUs it stays one launch.  Every grid
-    # must give the bits of the full-width grid, and those match the oracle.
+    # The one-tile-per-block plan: 12 M tiles x 4 N tiles of 128x256 = 48
+    # tiles.  On a 20-CU grid the two whole rounds (10 M tiles) run in one
+    # launch and the last 2 M tiles in a second launch of 128x128 tiles; on 7
+    # CUs it stays one launch.  Every grid must give the bits of the full-width
+    # grid, and those match the oracle.
     w, qa, sa, qb, sb = _contig_host(4, 1100, 1024, 512, seed=5, ue8m0=ue8m0)
     assert w.m_indices.size == 1536
     a = (upload_codes(qa), upload(sa))
@@ -93,7 +107,8 @@ def test_contiguous_ragged_last_round_split(ue8m0):
         dg.set_num_cus(cus)
         try:
             d = sentinel_like((qa.shape[0], qb.shape[1]))
-            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi)
+            with _contig_plan(2):
+                dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi)
             torch.cuda.synchronize()
         finally:
             dg.set_num_cus(0)
@@ -143,6 +158,99 @@ def test_contiguous_two_launch_plan_graph_replays_with_new_routing():
             assert_gemm_close(got[~pad], want[~pad], f"replay {rep}")
     finally:
         dg.set_num_cus(0)
+
+
+def _segments_layout(segments):
+    """m_indices from (group, blocks, valid rows of the last block) segments;
+    group -1 gives padding-only blocks."""
+    parts = []
+    for g, nb, last_valid in segments:
+        for b in range(nb):
+            valid = 128 if (b < nb - 1 or g < 0) else last_valid
+            parts.append(np.full(valid, g, np.int32))
+            parts.append(np.full(128 - valid, -1, np.int32))
+    return np.concatenate(parts)
+
+
+def _random_problem(m_total, groups, n, k, seed):
+    """Codes of N(0,1) * 32 values (torch's CPU E4M3 conversion, fast for big
+    layouts) and random power-of-two-ish scales.  Uniformly random codes would
+    span 2^35 in product magnitude, far beyond what quantized data holds."""
+    rng = np.random.default_rng(seed)
+
+    def codes(shape):
+        x = torch.from_numpy((rng.standard_normal(shape) * 32).astype(np.float32))
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    qa = codes((m_total, k))
+    sa = np.exp2(rng.uniform(-12, -4, size=(m_total, k // 128))).astype(np.float32)
+    qb = codes((groups, n, k))
+    sb = np.exp2(rng.uniform(-12, -4, size=(groups, (n + 127) // 128, k // 128))).astype(np.float32)
+    return qa, sa, qb, sb
+
+
+PAIR_LAYOUTS = {
+    # odd-aligned starts, segments of 1, 2, 3 blocks, a padding-only block
+    # between two blocks of one group, adjacent groups, a trailing single
+    "short_segments": [(0, 3, 100), (1, 1, 1), (2, 2, 128), (3, 5, 64), (-1, 1, 0), (3, 1, 7), (0, 2, 128),
+                       (1, 4, 90), (2, 1, 128)],
+    # long segments crossing the 32-block chunks each lane of the scan walks
+    "long_segments": [(g % 4, 17 + 7 * g, 128 - 9 * g) for g in range(8)] + [(-1, 2, 0)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAIR_LAYOUTS))
+def test_contiguous_pair_plan_layouts(name):
+    """Pairs of consecutive blocks of a group run as 256-row tiles, leftover
+    blocks as 128-row tiles: padding rows untouched, values within the oracle's
+    tolerance, and the same bits as the one-tile-per-block plan and as a narrow
+    grid (one workgroup walking every tile)."""
+    m_indices = _segments_layout(PAIR_LAYOUTS[name])
+    groups = 4
+    nb = m_indices.size // 128
+    assert nb >= 2 * groups
+    n, k = 264, 384
+    qa, sa, qb, sb = _random_problem(m_indices.size, groups, n, k, seed=nb)
+    with _contig_plan(1):
+        got = _gpu_contig(qa, sa, qb, sb, m_indices)
+    pad = m_indices < 0
+    assert np.all(got[pad] == SENTINEL), "padding rows written"
+    want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, m_indices)
+    assert_gemm_close(got[~pad], want[~pad], name)
+    with _contig_plan(2):
+        assert np.array_equal(_gpu_contig(qa, sa, qb, sb, m_indices), got)
+    try:
+        dg.set_num_cus(1)
+        with _contig_plan(1):
+            assert np.array_equal(_gpu_contig(qa, sa, qb, sb, m_indices), got)
+    finally:
+        dg.set_num_cus(0)
+
+
+@pytest.mark.parametrize("nblocks", [2048, 2049])
+def test_contiguous_pair_plan_largest_layout(nblocks):
+    """2048 blocks is the largest layout the paired plan takes (its tile list
+    lives in LDS); 2049 blocks runs the one-tile-per-block plan.  Segments of
+    1..11 blocks over 8 groups, cycling, so that pairs and singles cross every
+    32-block chunk of the device-side scan.  Sampled rows of every group."""
+    segs, total, i = [], 0, 0
+    while total < nblocks:
+        length = min(1 + (i * 7) % 11, nblocks - total)
+        segs.append((i % 8, length, 128 - (i * 13) % 128))
+        total += length
+        i += 1
+    m_indices = _segments_layout(segs)
+    assert m_indices.size == nblocks * 128
+    n, k = 64, 128
+    qa, sa, qb, sb = _random_problem(m_indices.size, 8, n, k, seed=nblocks)
+    with _contig_plan(1):          # taken up to 2048 blocks; beyond, plan 2 regardless
+        got = _gpu_contig(qa, sa, qb, sb, m_indices)
+    pad = m_indices < 0
+    assert np.all(got[pad] == SENTINEL), "padding rows written"
+    rows = np.nonzero(~pad)[0][::97]
+    want = ogemm.m_grouped_contiguous(qa[rows], sa[rows], qb, sb, m_indices[rows])
+    assert_gemm_close(got[rows], want, f"{nblocks} blocks")
+    assert bool(np.isfinite((got[~pad].astype(np.uint32) << 16).view(np.float32)).all()), "a valid row was not written"
 
 
 def test_contiguous_padding_block_skipped_and_hand_layout():

@@ -21,7 +21,9 @@ The JSON line also carries:
   Each shape also gets its roofline ceiling, min(FP8 peak, FLOPs / minimal
   bytes x HBM peak), and the cold rate as a percentage of that ceiling (the
   M <= 128 shapes are bound by streaming B, not by the MFMA);
-* ``cpu_baseline``: the CPU oracle timed on the full 4096x4096x7168 GEMM (4 runs);
+* ``cpu_baseline``: the CPU oracle on the whole dense workload (every GEMM at
+  full size), on group samples of the MoE workloads and a row sample of the
+  cast, with the CPU model, BLAS library and thread count;
 * ``extras``: the MoE workloads (contiguous G=8, masked G=16 with its decode
   variant, Zipf contiguous G=256 with power-of-two scales), each with the same
   ceiling, and the per-token cast of a bf16 [32768, 7168] activation in GB/s.
@@ -254,28 +256,104 @@ def bench_extras(dg, dev, reps):
     return out
 
 
-def cpu_baseline():
-    """The oracle as it stands, on the full 4096x4096x7168 GEMM of the workload (4 runs)."""
+def _host_info():
+    """CPU model, BLAS library and the threads it uses (threadpoolctl)."""
     from threadpoolctl import threadpool_info
-    from oracle import gemm as ogemm
-    from oracle import quant
-    m, n, k = 4096, 4096, 7168
-    idx = synth.config1_shapes().index((m, n, k))
-    w = synth.config1(idx)
-    qa, sa = quant.per_token_cast(w.a)
-    qb, sb = quant.per_block_cast(w.b)
-    del w
-    reps = 4
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        ogemm.gemm_nt(qa, sa, qb, sb)
-    dt = (time.perf_counter() - t0) / reps
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = max([i.get("num_threads", 1) for i in blas] or [1])
-    return {"value": 2.0 * m * n * k / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full {m}x{n}x{k} GEMM of the workload, {reps} times (decode, float64 BLAS matmul, "
-                      f"bf16 rounding): {dt:.2f} s each; BLAS threads {threads}, host cores "
-                      f"{len(os.sched_getaffinity(0))}"}
+    lib = ", ".join(sorted({"%s %s" % (i.get("internal_api", "?"), i.get("version", "")) for i in blas})) or "none"
+    return model, lib, int(threads)
+
+
+def cpu_baseline():
+    """The oracle as it stands (decode, float64 BLAS matmul, one bf16 rounding;
+    the quantizer for the cast), timed on the host cores.  The oracle's time
+    does not depend on the values, so the operands are random finite E4M3 codes
+    and random scales of each workload's exact shapes (drawing them is not
+    timed).  Dense step: every GEMM of the workload in full, once.  MoE
+    workloads: the oracle on a sample of groups, extrapolated by useful FLOPs.
+    Cast: a row sample of the bf16 [32768, 7168] activation."""
+    from oracle import gemm as ogemm
+    from oracle import quant
+    rng = np.random.default_rng(7)
+
+    def codes(shape):
+        return (rng.integers(0, 0x7F, size=shape, dtype=np.uint8) | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7))
+
+    def scales(shape):
+        return np.exp2(rng.uniform(-12, -4, size=shape)).astype(np.float32)
+
+    per = {}
+    # dense step, every GEMM in full
+    t_step, flops_step = 0.0, 0.0
+    for (m, n, k) in synth.config1_shapes():
+        qa, sa, qb, sb = codes((m, k)), scales((m, k // 128)), codes((n, k)), scales(((n + 127) // 128, k // 128))
+        t0 = time.perf_counter()
+        ogemm.gemm_nt(qa, sa, qb, sb)
+        t_step += time.perf_counter() - t0
+        flops_step += 2.0 * m * n * k
+        del qa, sa, qb, sb
+    per["dense_step"] = {"s": round(t_step, 3), "tflops": round(flops_step / t_step / 1e12, 4), "sample": "all 15 GEMMs"}
+    # config 0
+    qa, sa, qb, sb = codes((128, 512)), scales((128, 4)), codes((256, 512)), scales((2, 4))
+    t0 = time.perf_counter()
+    ogemm.gemm_nt(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    per["dense_128x256x512"] = {"s": round(dt, 5), "tflops": round(2.0 * 128 * 256 * 512 / dt / 1e12, 5)}
+
+    def grouped(name, counts, n, k, sample_groups, masked):
+        """oracle time on the rows of sample_groups, extrapolated by useful FLOPs"""
+        rows = [int(counts[g]) for g in sample_groups]
+        r = sum(rows)
+        qa, sa = codes((r, k)), scales((r, k // 128))
+        qb, sb = codes((len(rows), n, k)), scales((len(rows), (n + 127) // 128, k // 128))
+        t0 = time.perf_counter()
+        if masked:
+            mm = max(rows)
+            a3 = np.zeros((len(rows), mm, k), np.uint8)
+            s3 = np.ones((len(rows), mm, k // 128), np.float32)
+            ogemm.m_grouped_masked(a3, s3, qb, sb, np.array(rows, np.int32))
+        else:
+            mi = np.concatenate([np.full(c, i, np.int32) for i, c in enumerate(rows)])
+            ogemm.m_grouped_contiguous(qa, sa, qb, sb, mi)
+        dt = time.perf_counter() - t0
+        useful_sample = 2.0 * r * n * k
+        useful = 2.0 * int(np.sum(counts)) * n * k
+        per[name] = {"s_extrapolated": round(dt * useful / useful_sample, 3),
+                     "tflops": round(useful_sample / dt / 1e12, 4),
+                     "sample": "%d of %d groups (%d rows)" % (len(rows), len(counts), r)}
+
+    for idx, (n, k) in enumerate(synth.GROUPED_NK):
+        counts, _ = synth.config2_routing(idx)
+        grouped(f"contiguous_G8_{n}x{k}", counts, n, k, [0, 1], False)
+        mm = synth.config3_masked_m(idx)
+        grouped(f"masked_G16_{n}x{k}", mm, n, k, [int(np.argmax(mm)), 0], True)
+    counts, _ = synth.config4_routing()
+    n, k = synth.CONFIG4_NK
+    order = np.argsort(counts)
+    grouped("contiguous_zipf_G256_4096x7168", counts, n, k, [int(order[-1]), int(order[len(order) // 2]),
+                                                              int(order[0])], False)
+    # cast: 1024 rows of the bf16 activation (widened exactly to fp32)
+    x = (rng.standard_normal((1024, 7168)) * np.exp2(rng.uniform(-4, 4, (1024, 1)))).astype(np.float32)
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    t0 = time.perf_counter()
+    quant.per_token_cast(x)
+    dt = time.perf_counter() - t0
+    per["per_token_cast_bf16"] = {"gbs": round(x.size * (2 + 1 + 4 / 128) / dt / 1e9, 4),
+                                  "sample": "1024 of 32768 rows"}
+    model, lib, threads = _host_info()
+    return {"value": round(flops_step / t_step / 1e12, 4), "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": "the whole dense workload (all 15 GEMMs at full size, once) through the oracle: "
+                      "%.1f s; random E4M3 codes and scales of the exact shapes" % t_step,
+            "cpu_model": model, "blas": lib, "host_cores": len(os.sched_getaffinity(0)), "per_config": per}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.txt")

@@ -20,7 +20,12 @@ The JSON line also carries:
   around every launch, and cold-cache times (operands evicted before each run).
   Each shape also gets its roofline ceiling, min(FP8 peak, FLOPs / minimal
   bytes x HBM peak), and the cold rate as a percentage of that ceiling (the
-  M <= 128 shapes are bound by streaming B, not by the MFMA);
+  M <= 128 shapes are bound by streaming B, not by the MFMA).  The M <= 128
+  shapes also get ``us_cold_pipelined``: back-to-back launches over distinct
+  operand copies (> 512 MB in all, so every launch still reads HBM), which
+  removes the per-launch event overhead that dominates a single short launch;
+* ``event_floor_us``: the event time of a one-element fill kernel, the least an
+  event pair around any single launch measures here;
 * ``cpu_baseline``: the CPU oracle on the whole dense workload (every GEMM at
   full size), on group samples of the MoE workloads and a row sample of the
   cast, with the CPU model, BLAS library and thread count;
@@ -131,6 +136,31 @@ def event_time_ms(fn, reps, flush=None, warmup=5):
     return float(np.median(times))
 
 
+def event_floor_us(dev, reps=20):
+    """Event time of the smallest kernel (a one-element fill): what an event
+    pair around any single launch measures at least on this system."""
+    x = torch.empty(1, dtype=torch.float32, device=dev)
+    return event_time_ms(lambda: x.zero_(), reps) * 1e3
+
+
+def pipelined_cold_us(dg, a, b, d, min_bytes_total=600 << 20, reps=5):
+    """Per-launch time of R back-to-back launches of one GEMM, each on its own
+    copy of the operands, R copies spanning more than the 256 MB last-level
+    cache (and the flush) so that every launch reads cold operands."""
+    nbytes = a[0].numel() + b[0].numel() + 4 * (a[1].numel() + b[1].numel())
+    r = max(4, -(-min_bytes_total // nbytes))
+    copies = [((a[0].clone(), a[1].clone()), (b[0].clone(), b[1].clone()), torch.empty_like(d)) for _ in range(r)]
+    flush = Flusher(a[0].device)
+
+    def run():
+        for aa, bb, dd in copies:
+            dg.fp8_gemm_nt(aa, bb, dd)
+    ms = event_time_ms(run, reps, flush, warmup=2)
+    del copies, flush
+    torch.cuda.empty_cache()
+    return ms * 1e3 / r
+
+
 def bench_extras(dg, dev, reps):
     out = {}
     flush = Flusher(dev)
@@ -150,6 +180,7 @@ def bench_extras(dg, dev, reps):
             dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), q=qb[g], sf=sb[g])
         d = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
         mi = torch.from_numpy(m_indices).to(dev)
+        log(f"extras: contiguous G=8 {n}x{k}")
         ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((qa, sa), (qb, sb), d, mi), reps, flush)
         useful = 2.0 * int(counts.sum()) * n * k
         ceil = ceiling_tflops(useful, min_bytes(int(counts.sum()), n, k, 8))
@@ -173,6 +204,7 @@ def bench_extras(dg, dev, reps):
             dg.per_block_cast_fp8(synth.draw_weight_device(n, k, seed, g, dev), q=qb[g], sf=sb[g])
         d = torch.empty((16, 256, n), dtype=torch.bfloat16, device=dev)
         mm = torch.from_numpy(masked_m).to(dev)
+        log(f"extras: masked G=16 {n}x{k}")
         ms = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm, 128), reps, flush)
         useful = 2.0 * int(masked_m.sum()) * n * k
         b_bytes = 16 * n * k
@@ -194,6 +226,7 @@ def bench_extras(dg, dev, reps):
     tot_flops, t_fp32, t_packed = 0.0, 0.0, 0.0
     per = {}
     for (m, n, k) in shapes4k:
+        log(f"extras: dense {m}x{n}x{k}, power-of-two scales")
         seed = synth.seed_for(1, synth.config1_shapes().index((m, n, k)))
         a32 = synth.draw_activation_device(m, k, seed, dev)
         b32 = synth.draw_weight_device(n, k, seed, 0, dev)
@@ -214,6 +247,7 @@ def bench_extras(dg, dev, reps):
         "tflops_fp32_scales": tot_flops / t_fp32 / 1e9, "tflops_packed_ue8m0": tot_flops / t_packed / 1e9,
         "pct_fp8_peak_packed_ue8m0": 100 * tot_flops / t_packed / 1e9 / FP8_PEAK_TFLOPS, "per_shape": per}
     # --- Zipf contiguous G=256, power-of-two scales
+    log("extras: Zipf contiguous G=256")
     counts, m_indices = synth.config4_routing()
     n, k = synth.CONFIG4_NK
     seed = synth.seed_for(4, 0)
@@ -357,7 +391,19 @@ def cpu_baseline():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.txt")
-GEMM_SOURCE = os.path.join(ROOT, "moe_fp8_gemm_amd", "csrc", "gemm_fp8.hip")
+# The GEMM kernels' source: the kernel file and the two headers it includes.
+GEMM_SOURCES = [os.path.join(ROOT, "moe_fp8_gemm_amd", "csrc", f)
+                for f in ("gemm_fp8.hip", "dgfp8_device.h", "dgfp8_internal.h")]
+
+
+def gemm_source_sha256():
+    """sha256 of the GEMM kernel sources, concatenated in the order above."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_profile(cfg, shapes):
@@ -366,7 +412,6 @@ def measured_profile(cfg, shapes):
     copy) and the shader clock it ran at (GRBM_GUI_ACTIVE).  None when there is
     none for this instance and shape set or the kernel source has changed since
     the counters were taken."""
-    import hashlib
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -374,7 +419,7 @@ def measured_profile(cfg, shapes):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    sha = gemm_source_sha256()
     want_shapes = ",".join("%dx%dx%d" % s for s in shapes)
     if (kv.get("kernel_source_sha256") != sha or kv.get("tile") != "%dx%dx%d" % cfg
             or kv.get("shapes") != want_shapes):
@@ -509,7 +554,15 @@ def main():
         ceil = ceiling_tflops(flops[i], min_bytes(*shapes[i]))
         per_shape[i]["ceiling_tflops"] = ceil
         per_shape[i]["pct_of_ceiling_cold"] = 100 * per_shape[i]["tflops_cold"] / ceil
+        if shapes[i][0] <= 128:
+            # Back-to-back launches over enough distinct operand copies (> 512 MB
+            # in all) that every launch still reads its operands from HBM: the
+            # per-launch event overhead is paid once per batch, not per launch.
+            us = pipelined_cold_us(dg, a, b, d)
+            per_shape[i]["us_cold_pipelined"] = us
+            per_shape[i]["pct_of_ceiling_cold_pipelined"] = 100 * flops[i] / (us * 1e-6) / 1e12 / ceil
     del flush
+    floor_us = event_floor_us(dev)
     prof = measured_profile(dom_cfg, [shapes[i] for i in big])
     # The 5.0 PFLOP/s peak assumes 2.4 GHz (256 CUs x 8192 FP8 FLOP per clock);
     # the committed counter pass also gives the clock the kernel actually ran at.
@@ -543,6 +596,7 @@ def main():
                      "peak_at_profiled_sclk": round(peak_at_sclk, 1) if sclk else None,
                      "frac_at_profiled_sclk": round(achieved / peak_at_sclk, 4) if sclk else None},
         "per_shape": per_shape,
+        "event_floor_us": round(floor_us, 2),
     }
     if not args.no_extras:
         log("extras: MoE workloads and cast")

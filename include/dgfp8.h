@@ -370,6 +370,23 @@ dg_status dg_pack_ue8m0(const float* sf, int64_t sf_s0, int64_t sf_s1,
  */
 dg_status dg_set_contiguous_plan(int plan);
 
+/*
+ * Plan of the dense GEMM (dg_fp8_gemm_nt and its variants): instance < 0
+ * (default) picks the kernel instance and K split by the cost model; otherwise
+ * every following dense call in the process uses this instance, with `splits`
+ * K splits when the call has a workspace that holds them (else 1).  The
+ * workspace-size and tile-config queries report the forced plan.  Instances:
+ *   0 128x256, 1 128x128, 2 256x256, 3 128x64, 4 64x64  (LDS stages shared by
+ *     the workgroup's waves)
+ *   6 192x256
+ * A tuning and testing knob (the split changes the fp32 summation order, so
+ * results may differ in the last bits between plans).
+ * Errors: instance > 6 or splits < 1 -> DG_ERROR_INVALID_VALUE; instance 5
+ * (masked groups only), or splits > 1 with instance 2 or 6 (no split-K
+ * variant), or splits > 65536 -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_set_dense_plan(int instance, int splits);
+
 /* Row alignment of each group's segment in the contiguous layout: 128.
  * (Page ssnai.com DeepGEMM analysis: the alignment query for contiguous MoE.) */
 int dg_get_mk_alignment_for_contiguous_layout(void);

@@ -63,6 +63,7 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt_acc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
                             _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
     "dg_set_contiguous_plan": ([_i32], _i32),
+    "dg_set_dense_plan": ([_i32, _i32], _i32),
     "dg_fp8_gemm_nt_noalloc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
                                 _i64, _i64, _i64, _p], _i32),
 }
@@ -386,6 +387,12 @@ def set_contiguous_plan(plan: int) -> None:
     """Contiguous grouped GEMM plan: 0 cost model (default), 1 paired 256-row
     tiles + leftover 128-row blocks, 2 one tile per 128-row block.  Same bits."""
     _check(lib.dg_set_contiguous_plan(int(plan)), "dg_set_contiguous_plan")
+
+
+def set_dense_plan(instance: int, splits: int = 1) -> None:
+    """Force the dense GEMM's kernel instance and K splits (instance < 0: cost
+    model, the default).  Instance numbers as in dg_set_dense_plan."""
+    _check(lib.dg_set_dense_plan(int(instance), int(splits)), "dg_set_dense_plan")
 
 
 # The pages' names for the persistent-grid width (page ssnai.com DeepGEMM

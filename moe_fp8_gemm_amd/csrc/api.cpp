@@ -21,6 +21,8 @@ constexpr int kMaxDevices = 64;
 
 int g_num_cus_override = 0;
 int g_contig_plan = 0;   // 0: cost model, 1: paired plan, 2: one tile per 128-row block
+int g_dense_inst = -1;   // forced dense instance (-1: cost model) and its K splits
+int g_dense_splits = 1;
 int g_device_cus[kMaxDevices] = {0};
 
 // Compute units of the current device (ignores the override).
@@ -146,6 +148,13 @@ constexpr int kMinKbPerSplit = 2;   // at least 256 of K per unit
 // not depend on the grid-width override).
 DensePlan plan_dense(int64_t m, int64_t n, int64_t k, int cus, bool allow_split) {
   const int64_t kblocks = k / 128;
+  if (g_dense_inst >= 0) {
+    const int64_t s = allow_split ? std::min<int64_t>(g_dense_splits, kblocks) : 1;
+    const DensePlan forced = make_plan((GemmInstance)g_dense_inst, m, n, kblocks, s);
+    // one arrival counter per output tile
+    if (forced.splits > 1 && forced.tiles > kSplitCounters) return make_plan(forced.inst, m, n, kblocks, 1);
+    return forced;
+  }
   const DensePlan plain = make_plan(choose_dense(m, n, cus), m, n, kblocks, 1);
   if (plain.tiles * 2 > cus) return plain;
   DensePlan best = plain;
@@ -263,6 +272,23 @@ DG_EXPORT const char* dg_status_string(dg_status status) {
     case DG_ERROR_SCRATCH_LIMIT: return "DG_ERROR_SCRATCH_LIMIT";
   }
   return "DG_ERROR_UNKNOWN";
+}
+
+DG_EXPORT dg_status dg_set_dense_plan(int instance, int splits) {
+  if (instance < 0) {
+    g_dense_inst = -1;
+    g_dense_splits = 1;
+    return DG_SUCCESS;
+  }
+  if (instance >= kNumInstances || splits < 1) return DG_ERROR_INVALID_VALUE;
+  // the 64 x 256 instance serves masked groups only; 256 x 256 and 192 x 256
+  // have no split-K variant
+  if (instance == kInstDecode) return DG_ERROR_NOT_SUPPORTED;
+  if ((instance == kInstHuge || instance == kInstTall) && splits > 1) return DG_ERROR_NOT_SUPPORTED;
+  if (splits > kSplitCounters) return DG_ERROR_NOT_SUPPORTED;
+  g_dense_inst = instance;
+  g_dense_splits = splits;
+  return DG_SUCCESS;
 }
 
 DG_EXPORT size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {

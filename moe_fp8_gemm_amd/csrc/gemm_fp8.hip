@@ -895,7 +895,7 @@ InstanceInfo instance_info(GemmInstance inst) {
     case kInstMid: return {CfgMid::BM, CfgMid::BN, CfgMid::kOcc};
     case kInstDecode: return {CfgDecode::BM, CfgDecode::BN, CfgDecode::kOcc};
     case kInstTall: return {CfgTall::BM, CfgTall::BN, CfgTall::kOcc};
-    default: return {0, 0};
+    default: return {0, 0, 0};
   }
 }
 

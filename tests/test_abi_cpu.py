@@ -205,6 +205,26 @@ def test_grid_width_setting_and_the_pages_names():
         dg.set_num_cus(0)
 
 
+def test_forced_dense_plan_is_reported_and_checked():
+    import moe_fp8_gemm_amd as dg
+    try:
+        dg.set_dense_plan(3, 5)                       # 128 x 64 tiles, 5 K splits
+        assert dg.tile_config(100, 520, 1408) == (128, 64, 4)    # 11 blocks: 3 per split -> 4 splits
+        assert dg.tile_config(100, 520, 1408, workspace=False) == (128, 64, 1)
+        assert dg.workspace_size(100, 520, 1408) == 256 * 1024 + 1 * 9 * 4 * 128 * 64 * 4
+        dg.set_dense_plan(4, 100)                     # more splits than K blocks: one block each
+        assert dg.tile_config(64, 256, 640) == (64, 64, 5)
+    finally:
+        dg.set_dense_plan(-1)
+    for inst, splits, status in [(7, 1, dg.DG_ERROR_INVALID_VALUE), (1, 0, dg.DG_ERROR_INVALID_VALUE),
+                                 (5, 1, dg.DG_ERROR_NOT_SUPPORTED), (2, 2, dg.DG_ERROR_NOT_SUPPORTED),
+                                 (6, 3, dg.DG_ERROR_NOT_SUPPORTED)]:
+        with pytest.raises(dg.DgError) as e:
+            dg.set_dense_plan(inst, splits)
+        assert e.value.status == status
+    dg.set_dense_plan(-1)
+
+
 # ------------------------------------------------------------------ binding: scale shapes
 
 def test_binding_rejects_scale_tensors_of_the_wrong_shape():

@@ -22,10 +22,11 @@ The JSON line also carries:
   bytes x HBM peak), and the cold rate as a percentage of that ceiling (the
   M <= 128 shapes are bound by streaming B, not by the MFMA).  The M <= 128
   shapes also get ``us_cold_pipelined``: back-to-back launches over distinct
-  operand copies (> 512 MB in all, so every launch still reads HBM), which
-  removes the per-launch event overhead that dominates a single short launch;
-* ``event_floor_us``: the event time of a one-element fill kernel, the least an
-  event pair around any single launch measures here;
+  operand copies (> 512 MB in all, so every launch still reads HBM), replayed
+  from a HIP graph, which removes the per-launch event overhead of a single
+  short launch;
+* ``event_floor_us``: the event time of a one-element fill kernel measured like
+  the cold times, the least an event pair around one launch reads here;
 * ``cpu_baseline``: the CPU oracle on the whole dense workload (every GEMM at
   full size), on group samples of the MoE workloads and a row sample of the
   cast, with the CPU model, BLAS library and thread count;
@@ -137,26 +138,40 @@ def event_time_ms(fn, reps, flush=None, warmup=5):
 
 
 def event_floor_us(dev, reps=20):
-    """Event time of the smallest kernel (a one-element fill): what an event
-    pair around any single launch measures at least on this system."""
+    """Event time of the smallest kernel (a one-element fill), measured the way
+    the cold per-shape times are (after the cache-evicting read, so the host
+    has queued the kernel before the GPU reaches it): the least an event pair
+    around one launch reads here."""
     x = torch.empty(1, dtype=torch.float32, device=dev)
-    return event_time_ms(lambda: x.zero_(), reps) * 1e3
+    flush = Flusher(dev)
+    us = event_time_ms(lambda: x.zero_(), reps, flush) * 1e3
+    del flush
+    return us
 
 
 def pipelined_cold_us(dg, a, b, d, min_bytes_total=600 << 20, reps=5):
     """Per-launch time of R back-to-back launches of one GEMM, each on its own
     copy of the operands, R copies spanning more than the 256 MB last-level
-    cache (and the flush) so that every launch reads cold operands."""
+    cache (and the flush) so that every launch reads cold operands.  The R
+    launches are captured once as a HIP graph and replayed, so host-side call
+    overhead does not enter the time."""
     nbytes = a[0].numel() + b[0].numel() + 4 * (a[1].numel() + b[1].numel())
     r = max(4, -(-min_bytes_total // nbytes))
     copies = [((a[0].clone(), a[1].clone()), (b[0].clone(), b[1].clone()), torch.empty_like(d)) for _ in range(r)]
-    flush = Flusher(a[0].device)
+    m, n, k = a[0].shape[0], b[0].shape[0], a[0].shape[1]
+    ws = torch.zeros(max(dg.workspace_size(m, n, k), 16), dtype=torch.uint8, device=d.device)
 
     def run():
         for aa, bb, dd in copies:
-            dg.fp8_gemm_nt(aa, bb, dd)
-    ms = event_time_ms(run, reps, flush, warmup=2)
-    del copies, flush
+            dg.fp8_gemm_nt(aa, bb, dd, workspace=ws)
+    run()                                   # outside the capture: first-call set-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    flush = Flusher(a[0].device)
+    ms = event_time_ms(graph.replay, reps, flush, warmup=2)
+    del copies, flush, graph, ws
     torch.cuda.empty_cache()
     return ms * 1e3 / r
 
@@ -558,6 +573,7 @@ def main():
             # Back-to-back launches over enough distinct operand copies (> 512 MB
             # in all) that every launch still reads its operands from HBM: the
             # per-launch event overhead is paid once per batch, not per launch.
+            # The flush object above stays alive; this one adds 1 GiB briefly.
             us = pipelined_cold_us(dg, a, b, d)
             per_shape[i]["us_cold_pipelined"] = us
             per_shape[i]["pct_of_ceiling_cold_pipelined"] = 100 * flops[i] / (us * 1e-6) / 1e12 / ceil

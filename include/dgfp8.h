@@ -201,9 +201,15 @@ dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, size_t ws_
  * every row with m_indices >= 0 has the same value, which lies in
  * [0, num_groups).  The group of a block is read from its first row; a block
  * whose first row is -1 is skipped entirely.
- * The work is one kernel launch, or two on the same stream when the tiles end
- * in a thinly filled last round (the rows of the whole rounds first, then the
- * remaining rows on narrower tiles); the results do not depend on the split.
+ * The work is one or two kernel launches on the same stream, planned from the
+ * sizes alone (the host never reads m_indices, so the call can be captured in
+ * a graph): when groups average two or more 128-row blocks, pairs of
+ * consecutive blocks of one group run as 256-row tiles and the blocks left
+ * over as 128-row tiles in a second launch, both tile lists built on the
+ * device; otherwise one tile per block, split into two launches when the tiles
+ * end in a thinly filled last round.  Every row is computed with the same
+ * operations in all of these plans, so the results do not depend on the plan
+ * or on dg_set_num_cus.  No K is split (see the _ws variant).
  * Errors: m_total % 128 != 0 -> DG_ERROR_MISALIGNED_LAYOUT.
  * Page juejin.cn, sections 3 and 4(3) (M-only grouping, contiguous layout
  * aligned to the M block); page "GitHub 推荐…", 风险与不足 (128-row padding).
@@ -325,6 +331,54 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, int64_t lda,
                                                     const int32_t* m_indices, int64_t m_total,
                                                     int64_t n, int64_t k, int num_groups,
                                                     void* stream);
+
+/*
+ * Contiguous grouped GEMM as dg_m_grouped_fp8_gemm_nt_contiguous, with a
+ * split-K workspace (caller-owned, 16-byte aligned, same contract as the dense
+ * one: the first 256 KiB are arrival counters, zero before first use and left
+ * zero by every completed call; calls that may overlap need distinct
+ * workspaces).  When the paired plan runs and ws_bytes is at least
+ * dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size(...), the second launch
+ * (the blocks no pair covers, typically one per group) splits K over the CUs
+ * its few tiles would leave idle: the kernel picks the split from the number
+ * of leftover blocks it finds, so the call stays graph-capturable.  Each split
+ * sums its K range in order and the last to arrive adds the fp32 partial tiles
+ * in split order, so results are deterministic and independent of
+ * dg_set_num_cus; rows of leftover blocks may differ from the unsplit call in
+ * the last bits, rows of paired blocks do not.  With ws null or too small the
+ * call behaves as dg_m_grouped_fp8_gemm_nt_contiguous.
+ * Errors: as dg_m_grouped_fp8_gemm_nt_contiguous; ws not 16-byte aligned ->
+ * DG_ERROR_NOT_SUPPORTED.
+ * Splitting K over workgroups is this library's addition for a 256-CU device
+ * (the pages only note low efficiency for thin shapes: page "企业官网建设流程全解析",
+ * sections 4.3 and 5.4).
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ws(const void* a, int64_t lda,
+                                                 const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                                 const void* b, int64_t ldb, int64_t b_group_stride,
+                                                 const float* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                                 int64_t sfb_group_stride,
+                                                 void* d, int64_t ldd,
+                                                 const int32_t* m_indices, int64_t m_total,
+                                                 int64_t n, int64_t k, int num_groups,
+                                                 void* ws, size_t ws_bytes, void* stream);
+
+/* As dg_m_grouped_fp8_gemm_nt_contiguous_ws with packed UE8M0 scales. */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_ws(const void* a, int64_t lda,
+                                                       const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+                                                       const void* b, int64_t ldb, int64_t b_group_stride,
+                                                       const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk,
+                                                       int64_t sfb_group_stride,
+                                                       void* d, int64_t ldd,
+                                                       const int32_t* m_indices, int64_t m_total,
+                                                       int64_t n, int64_t k, int num_groups,
+                                                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the _ws contiguous calls can use for this problem (0: the
+ * plan never splits K).  Non-positive sizes, k % 128 != 0, m_total % 128 != 0 or
+ * num_groups < 1 give 0. */
+size_t dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size(int64_t m_total, int64_t n, int64_t k,
+                                                          int num_groups);
 
 /* Masked grouped GEMM as dg_m_grouped_fp8_gemm_nt_masked with packed UE8M0
  * scales (group strides in int32 elements). */

@@ -63,6 +63,13 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt_acc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
                             _i64, _i64, _i64, _p, ctypes.c_size_t, _p], _i32),
     "dg_set_contiguous_plan": ([_i32], _i32),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size": ([_i64, _i64, _i64, _i32], ctypes.c_size_t),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ws": ([_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64,
+                                                _p, _i64, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_size_t, _p],
+                                               _i32),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_ws": ([_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                      _i64, _p, _i64, _p, _i64, _i64, _i64, _i32, _p,
+                                                      ctypes.c_size_t, _p], _i32),
     "dg_set_dense_plan": ([_i32, _i32], _i32),
     "dg_fp8_gemm_nt_noalloc": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
                                 _i64, _i64, _i64, _p], _i32),
@@ -181,6 +188,20 @@ def _auto_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
+def _workspace_arg(workspace, device: torch.device, need: int) -> Tuple[int, int]:
+    """(pointer, bytes) of the split-K workspace argument: "auto" -> the cached
+    per-(device, stream) buffer when the problem can use one, None -> none."""
+    if isinstance(workspace, str):
+        if workspace != _AUTO:
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        workspace = _auto_workspace(device, need) if need > 0 else None
+    if workspace is None:
+        return 0, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
                 d: torch.Tensor, c: Optional[torch.Tensor] = None, workspace=_AUTO) -> torch.Tensor:
     """d[m, n] = bf16( A . B^T [+ c] ) with per-(row, 128-K) A scales and per-128x128 B scales.
@@ -202,16 +223,7 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
     if qb.shape[1] != k or d.shape != (m, n):
         raise ValueError("shape mismatch")
     _check_scale_shapes(sa, sb, (), m, n, k, _packed(sa, sb))
-    if isinstance(workspace, str):
-        if workspace != _AUTO:
-            raise ValueError("workspace must be 'auto', None or a tensor")
-        need = workspace_size(m, n, k)
-        workspace = _auto_workspace(d.device, need) if need > 0 else None
-    ws_ptr, ws_bytes = 0, 0
-    if workspace is not None:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise TypeError("workspace must be a contiguous device tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_arg(workspace, d.device, workspace_size(m, n, k))
     packed = _packed(sa, sb)
     if c is not None:
         if packed:
@@ -254,10 +266,20 @@ def fp8_gemm_nt_noalloc(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Ten
     return d
 
 
-def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
+def contiguous_workspace_size(m_total: int, n: int, k: int, num_groups: int) -> int:
+    """Bytes of split-K workspace m_grouped_fp8_gemm_nt_contiguous can use (0: never splits)."""
+    return int(lib.dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size(int(m_total), int(n), int(k),
+                                                                       int(num_groups)))
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor,
+                                     workspace=_AUTO) -> torch.Tensor:
     """Contiguous MoE layout: a = (codes [m_total, k], sfa [m_total, k/128]),
     b = (codes [G, n, k], sfb [G, ceil(n/128), k/128]), d bf16 [m_total, n],
-    m_indices int32 [m_total] (-1 on padding rows, which are left untouched)."""
+    m_indices int32 [m_total] (-1 on padding rows, which are left untouched).
+    ``workspace`` as for fp8_gemm_nt ("auto", None, or a zero-initialised uint8
+    device tensor of at least ``contiguous_workspace_size(...)`` bytes): with
+    one, the blocks that the paired plan leaves to its second launch split K."""
     (qa, sa), (qb, sb) = a, b
     _codes(qa, "a"); _codes(qb, "b"); _scales(sa, "sfa"); _scales(sb, "sfb"); _out_bf16(d, "d")
     if m_indices.dtype != torch.int32 or not m_indices.is_cuda:
@@ -273,12 +295,14 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     _check_scale_shapes(sa, sb[0], (), m_total, n, k, _packed(sa, sb))
     if sb.shape[0] != g:
         raise ValueError(f"sfb has {sb.shape[0]} groups, b has {g}")
-    fn = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if _packed(sa, sb) else lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    ws_ptr, ws_bytes = _workspace_arg(workspace, d.device, contiguous_workspace_size(m_total, n, k, g))
+    fn = (lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_ws if _packed(sa, sb)
+          else lib.dg_m_grouped_fp8_gemm_nt_contiguous_ws)
     _check(fn(
         qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), sa.stride(1),
         qb.data_ptr(), qb.stride(1), qb.stride(0),
         sb.data_ptr(), sb.stride(1), sb.stride(2), sb.stride(0),
-        d.data_ptr(), d.stride(0), m_indices.data_ptr(), m_total, n, k, g, _stream()),
+        d.data_ptr(), d.stride(0), m_indices.data_ptr(), m_total, n, k, g, ws_ptr or None, ws_bytes, _stream()),
         "dg_m_grouped_fp8_gemm_nt_contiguous")
     return d
 

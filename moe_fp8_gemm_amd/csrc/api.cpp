@@ -228,18 +228,50 @@ double contig_plan_cost(const ContigPlan& pl, int64_t m_total, int64_t n, int cu
          0.2 * instance_info(pl.head).bm * instance_info(pl.head).bn * area_factor(pl.head);
 }
 
+// Split of the paired plan's second launch (the blocks no pair covers): the
+// kernel picks s = min(cap, units / (listed blocks x N tiles)) on the device, so
+// the partial tiles never exceed `units` (the CU count, as for the dense
+// split-K plans).  Needs one arrival counter per (listed block, N tile) for up
+// to min(groups, blocks) listed blocks.
+struct ContigSplit {
+  bool ok;          // the split is possible for this problem
+  int units, cap;
+  int64_t ws_bytes; // workspace it needs
+};
+
+ContigSplit contig_split(GemmInstance si, int64_t nblocks, int64_t n, int64_t k, int num_groups, int cus) {
+  const InstanceInfo info = instance_info(si);
+  ContigSplit cs{false, cus * info.occ, (int)std::min<int64_t>(k / 128 / kMinKbPerSplit, 64), 0};
+  const int64_t max_listed = std::min<int64_t>(num_groups, nblocks);
+  cs.ok = cs.cap >= 2 && max_listed * ceil_div(n, info.bn) <= kSplitCounters;
+  cs.ws_bytes = kSplitCounterBytes + (int64_t)cs.units * info.bm * info.bn * (int64_t)sizeof(float);
+  return cs;
+}
+
 // Paired contiguous plan (see grouped_contiguous).  The host does not know the
 // routing, so the pair count is estimated: half of the groups end in a single
-// block.  Returns the instance for the single blocks and the estimated cost.
-GemmInstance paired_singles_instance(int64_t nblocks, int64_t n, int num_groups, int cus, double* cost) {
+// block.  Returns the instance for the single blocks and the estimated cost;
+// with `split`, the single blocks' launch splits K over the idle CUs.
+GemmInstance paired_singles_instance(int64_t nblocks, int64_t n, int64_t k, int num_groups, int cus, bool split,
+                                     double* cost) {
   const double singles = (double)std::min<int64_t>(num_groups, nblocks) / 2.0;
   const int64_t single_rows = (int64_t)(singles + 0.5) * 128;
   const int64_t pair_rows = (nblocks * 128 - single_rows) / 256 * 256;
   const GemmInstance si = instance_cost(kInstMid, single_rows, 0, n, cus) <=
                                   instance_cost(kInstLarge, single_rows, 0, n, cus)
                               ? kInstMid : kInstLarge;
-  *cost = instance_cost(kInstHuge, pair_rows, 0, n, cus) + instance_cost(si, single_rows, 0, n, cus) +
-          0.2 * instance_info(si).bm * instance_info(si).bn * area_factor(si);
+  const InstanceInfo info = instance_info(si);
+  const double round = (double)info.bm * info.bn * area_factor(si);
+  double singles_cost = instance_cost(si, single_rows, 0, n, cus);
+  const ContigSplit cs = contig_split(si, nblocks, n, k, num_groups, cus);
+  if (split && cs.ok && single_rows > 0) {
+    // s splits: ceil(tiles * s / cus) rounds of 1/s of a tile's K each, plus a
+    // tenth of a round for the partial-tile hand-off
+    const int64_t tiles = single_rows / 128 * ceil_div(n, info.bn);
+    const int64_t sp = std::max<int64_t>(1, std::min<int64_t>(cs.cap, cs.units / std::max<int64_t>(tiles, 1)));
+    if (sp > 1) singles_cost = (double)ceil_div(tiles * sp, cus) * round / (double)sp + 0.1 * round;
+  }
+  if (cost) *cost = instance_cost(kInstHuge, pair_rows, 0, n, cus) + singles_cost + 0.2 * round;
   return si;
 }
 
@@ -390,11 +422,39 @@ DG_EXPORT dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa,
 
 namespace {
 
+// Which contiguous plan runs (see grouped_contiguous).  Paired or not, and the
+// split, follow the problem, the hardware CU count and the workspace bytes
+// available, never the grid-width override: the split changes the summation
+// order of the rows it covers.  The one-launch-or-two choice of the unpaired
+// plan follows the grid width (it changes no bit).
+struct ContigDecision {
+  bool paired, split;
+  GemmInstance single;
+  ContigPlan plain;   // the unpaired plan for the current grid width
+};
+
+ContigDecision decide_contiguous(int64_t m_total, int64_t n, int64_t k, int num_groups, size_t ws_bytes) {
+  const int cus = hw_cus();
+  const int64_t nblocks = m_total / kContiguousAlignment;
+  ContigDecision dec{false, false, kInstMid, plan_contiguous(m_total, n, device_cus())};
+  if (nblocks > kMaxContigPairBlocks || g_contig_plan == 2) return dec;
+  const GemmInstance si_est = paired_singles_instance(nblocks, n, k, num_groups, cus, false, nullptr);
+  const ContigSplit cs = contig_split(si_est, nblocks, n, k, num_groups, cus);
+  const bool split = cs.ok && (int64_t)ws_bytes >= cs.ws_bytes;
+  double paired_cost = 0.0;
+  dec.single = paired_singles_instance(nblocks, n, k, num_groups, cus, split, &paired_cost);
+  // the model must predict a clear gain: within 10% the two plans measure alike
+  dec.paired = g_contig_plan == 1 ||
+               paired_cost < 0.9 * contig_plan_cost(plan_contiguous(m_total, n, cus), m_total, n, cus);
+  dec.split = dec.paired && split;
+  return dec;
+}
+
 dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk,
                              const void* b, int64_t ldb, int64_t b_group_stride, const void* sfb, int64_t sfb_sn,
                              int64_t sfb_sk, int64_t sfb_group_stride, void* d, int64_t ldd,
                              const int32_t* m_indices, int64_t m_total, int64_t n, int64_t k, int num_groups,
-                             void* stream, bool packed) {
+                             void* ws, size_t ws_bytes, void* stream, bool packed) {
   if (m_total < 0 || n < 0 || k < 0 || num_groups < 1) return DG_ERROR_INVALID_VALUE;
   if (b_group_stride < 0 || sfb_group_stride < 0) return DG_ERROR_INVALID_VALUE;
   if (m_total % kContiguousAlignment != 0) return DG_ERROR_MISALIGNED_LAYOUT;
@@ -404,6 +464,7 @@ dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_
   if (st != DG_SUCCESS) return st;
   if (b_group_stride % 16 != 0 || !aligned(m_indices, 4)) return DG_ERROR_NOT_SUPPORTED;
   if (!offsets_fit(m_total, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
+  if (ws && !aligned(ws, 16)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a); p.lda = lda;
   p.sfa = sf_ptr(sfa); p.sfa_sm = sfa_sm; p.sfa_sk = sfa_sk;
@@ -420,23 +481,35 @@ dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_
   // launch.  Both launches find their tiles on the device from m_indices, so
   // the plan needs no host read and stays graph-capturable.  Each row's result
   // is computed the same way whatever its tile, so no bit changes.
+  //
+  // With a workspace the second launch splits K over the CUs its few tiles
+  // leave idle (the split is chosen on the device from the listed blocks).
+  // The plan follows the hardware CU count, never the grid-width override, so
+  // the results (which the split's summation order affects) do not depend on
+  // the override.
   const int64_t nblocks = m_total / kContiguousAlignment;
-  const ContigPlan pl = plan_contiguous(m_total, n, device_cus());
-  if (nblocks <= kMaxContigPairBlocks && g_contig_plan != 2) {
-    double paired_cost = 0.0;
-    const GemmInstance single = paired_singles_instance(nblocks, n, num_groups, device_cus(), &paired_cost);
-    // the model must predict a clear gain: within 10% the two plans measure alike
-    if (g_contig_plan == 1 || paired_cost < 0.9 * contig_plan_cost(pl, m_total, n, device_cus())) {
-      const InstanceInfo hi = instance_info(kInstHuge);
-      GemmParams pp = p;
-      pp.contig_mode = 1;
-      st = launch(kInstHuge, kContiguous, pp, (nblocks / 2) * ceil_div(n, hi.bn), s);
-      if (st != DG_SUCCESS) return st;
-      GemmParams ps = p;
-      ps.contig_mode = 2;
-      return launch(single, kContiguous, ps, nblocks * ceil_div(n, instance_info(single).bn), s);
+  const ContigDecision dec = decide_contiguous(m_total, n, k, num_groups, ws != nullptr ? ws_bytes : 0);
+  if (dec.paired) {
+    const InstanceInfo hi = instance_info(kInstHuge);
+    GemmParams pp = p;
+    pp.contig_mode = 1;
+    st = launch(kInstHuge, kContiguous, pp, (nblocks / 2) * ceil_div(n, hi.bn), s);
+    if (st != DG_SUCCESS) return st;
+    GemmParams ps = p;
+    ps.contig_mode = 2;
+    const int64_t tiles_bound = std::min<int64_t>(num_groups, nblocks) * ceil_div(n, instance_info(dec.single).bn);
+    if (dec.split) {
+      const ContigSplit cs = contig_split(dec.single, nblocks, n, k, num_groups, hw_cus());
+      ps.counters = static_cast<int*>(ws);
+      ps.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kSplitCounterBytes);
+      ps.splits = cs.cap;
+      ps.kb_per_split = (int)(k / 128);
+      ps.contig_split_units = cs.units;
+      return launch(dec.single, kContiguousSplitK, ps, std::max<int64_t>(tiles_bound, cs.units), s);
     }
+    return launch(dec.single, kContiguous, ps, tiles_bound, s);
   }
+  const ContigPlan pl = dec.plain;
   const InstanceInfo hi = instance_info(pl.head);
   GemmParams ph = p;
   ph.m = pl.head_rows;
@@ -463,7 +536,8 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous(
     void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
     int64_t n, int64_t k, int num_groups, void* stream) {
   return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
-                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, stream, false);
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, nullptr, 0, stream,
+                            false);
 }
 
 DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
@@ -473,7 +547,39 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
     void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
     int64_t n, int64_t k, int num_groups, void* stream) {
   return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
-                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, stream, true);
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, nullptr, 0, stream,
+                            true);
+}
+
+DG_EXPORT size_t dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size(int64_t m_total, int64_t n, int64_t k,
+                                                                    int num_groups) {
+  if (m_total <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || num_groups < 1) return 0;
+  if (m_total % kContiguousAlignment != 0) return 0;
+  const ContigDecision dec = decide_contiguous(m_total, n, k, num_groups, (size_t)INT64_MAX);
+  if (!dec.split) return 0;
+  return (size_t)contig_split(dec.single, m_total / kContiguousAlignment, n, k, num_groups, hw_cus()).ws_bytes;
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ws(
+    const void* a, int64_t lda, const float* sfa, int64_t sfa_sm, int64_t sfa_sk,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const float* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
+    int64_t n, int64_t k, int num_groups, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, ws, ws_bytes, stream,
+                            false);
+}
+
+DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_ws(
+    const void* a, int64_t lda, const int32_t* sfa, int64_t sfa_sm, int64_t sfa_sk,
+    const void* b, int64_t ldb, int64_t b_group_stride,
+    const int32_t* sfb, int64_t sfb_sn, int64_t sfb_sk, int64_t sfb_group_stride,
+    void* d, int64_t ldd, const int32_t* m_indices, int64_t m_total,
+    int64_t n, int64_t k, int num_groups, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_contiguous(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, b_group_stride, sfb, sfb_sn, sfb_sk,
+                            sfb_group_stride, d, ldd, m_indices, m_total, n, k, num_groups, ws, ws_bytes, stream,
+                            true);
 }
 
 namespace {

@@ -10,7 +10,10 @@ namespace dgfp8 {
 
 // kDenseSplitK: dense GEMM whose K range is split over several workgroups per
 // output tile (small M); partial sums go through a workspace.
-enum Variant : int { kDense = 0, kContiguous = 1, kMasked = 2, kDenseSplitK = 3 };
+// kContiguousSplitK: the contiguous GEMM on the 128-row blocks listed on the
+// device (contig_mode 2), with a K split the kernel derives from the number of
+// listed blocks (see contig_split_units).
+enum Variant : int { kDense = 0, kContiguous = 1, kMasked = 2, kDenseSplitK = 3, kContiguousSplitK = 4 };
 
 // Everything a GEMM launch needs.  Pointers are device addresses; strides are
 // in elements (bytes for the E4M3 operands).
@@ -45,6 +48,11 @@ struct GemmParams {
   // consecutive blocks of one group; 2 = 128-row tiles on the blocks no pair
   // covers (tile lists built on the device from m_indices)
   int contig_mode;
+  // kContiguousSplitK only: the K split s is the largest with
+  // (listed blocks) x (N tiles) x s <= contig_split_units, at most `splits`
+  // (and at most the K blocks); the workspace holds contig_split_units partial
+  // tiles.  A host constant, so the split never depends on the grid width.
+  int contig_split_units;
 };
 
 // Largest number of 128-row blocks (m_total / 128) a paired contiguous plan takes.

@@ -484,8 +484,13 @@ gemm_kernel(GemmParams p) {
   const uint32_t off1 = r16 * kKBlock + (((2 * q + 1) ^ swz16(r16)) << 4);
 
   // ---- tile space
+  constexpr bool kSplit = V == kDenseSplitK || V == kContiguousSplitK;
+  constexpr bool kContig = V == kContiguous || V == kContiguousSplitK;
   __shared__ int masked_prefix[V == kMasked ? kMaxMaskedGroups + 1 : 1];
   int tiles_m = 0, num_tiles = 0;
+  // K split of a split variant: units (tile, split) with kb_per_split K blocks each
+  int splits = kSplit ? p.splits : 1;
+  int kb_per_split = p.kb_per_split;
   if constexpr (V == kMasked) {
     // Exclusive prefix of per-group M-tile counts, from masked_m on the device.
     if (wave == 0) {
@@ -519,16 +524,27 @@ gemm_kernel(GemmParams p) {
     num_tiles = masked_prefix[kMaxMaskedGroups] * tiles_n;
   } else {
     tiles_m = (int)((p.m + C::BM - 1) / C::BM);
-    num_tiles = tiles_m * tiles_n * (V == kDenseSplitK ? p.splits : 1);
+    num_tiles = tiles_m * tiles_n * splits;
   }
-  __shared__ int16_t contig_list[V == kContiguous ? kMaxContigBlocks : 1];
+  __shared__ int16_t contig_list[kContig ? kMaxContigBlocks : 1];
   __shared__ int contig_count;
-  if constexpr (V == kContiguous) {
+  if constexpr (kContig) {
     if (p.contig_mode != 0) {
       if (wave == 0) contig_tile_list(p, lane, (DG_LAS int16_t*)contig_list, (DG_LAS int*)&contig_count);
       __syncthreads();
       tiles_m = contig_count;
-      num_tiles = tiles_m * tiles_n;
+      if constexpr (V == kContiguousSplitK) {
+        // As many splits as keep the units within contig_split_units (every
+        // workgroup computes the same value from the same list).
+        const int tiles = tiles_m * tiles_n;
+        int s = tiles > 0 ? p.contig_split_units / tiles : 1;
+        s = s < p.splits ? s : p.splits;
+        s = s < kblocks ? s : kblocks;
+        s = s > 1 ? s : 1;
+        kb_per_split = (kblocks + s - 1) / s;
+        splits = (kblocks + kb_per_split - 1) / kb_per_split;
+      }
+      num_tiles = tiles_m * tiles_n * splits;
     }
   }
 
@@ -561,15 +577,15 @@ gemm_kernel(GemmParams p) {
         int mm = p.masked_m[g];
         mm = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
         m_limit = mm;
-      } else if constexpr (V == kDenseSplitK) {
+      } else if constexpr (kSplit) {
         // consecutive units are the splits of one output tile: they run together
-        split = tile % p.splits;
-        raster(tile / p.splits, tiles_m, tiles_n, mt, nt);
+        split = tile % splits;
+        raster(tile / splits, tiles_m, tiles_n, mt, nt);
       } else {
         raster(tile, tiles_m, tiles_n, mt, nt);
       }
       int64_t m0 = (int64_t)mt * C::BM;
-      if constexpr (V == kContiguous) {
+      if constexpr (kContig) {
         if (p.contig_mode != 0) m0 = (int64_t)contig_list[mt] * kKBlock;   // listed block
         g = p.m_indices[m0];
         if (g < 0) return false;                // whole block is padding
@@ -633,9 +649,9 @@ gemm_kernel(GemmParams p) {
       }
 
       int kbs = kblocks;   // K blocks of this unit
-      if constexpr (V == kDenseSplitK) {
-        const int kb0 = split * p.kb_per_split;
-        kbs = min(p.kb_per_split, kblocks - kb0);
+      if constexpr (kSplit) {
+        const int kb0 = split * kb_per_split;
+        kbs = min(kb_per_split, kblocks - kb0);
         t.a_base += (int64_t)kb0 * kKBlock;
         t.b_base += (int64_t)kb0 * kKBlock;
         if constexpr (!C::kPackedSf) t.s_src += (int64_t)kb0 * t.s_kstride;
@@ -656,7 +672,7 @@ gemm_kernel(GemmParams p) {
     for (int ms = 0; ms < C::MS; ++ms) {
       const int64_t row = m0 + wr * C::WM + ms * 16 + (tl & 15);
       bool ok = row < m_limit;
-      if constexpr (V == kContiguous) ok = ok && (p.m_indices[row] >= 0);
+      if constexpr (kContig) ok = ok && (p.m_indices[row] >= 0);
       okm |= (ok ? 1u : 0u) << ms;
     }
     s.okmask = okm;
@@ -745,7 +761,7 @@ gemm_kernel(GemmParams p) {
     }
     Tile nxt;
     const int ntile = next_tile(tile + gridDim.x, nxt);
-    if constexpr (V == kDenseSplitK) {
+    if (kSplit && splits > 1) {
       // Publish this unit's partial tile, count arrivals; the last unit of the
       // output tile adds all partials in split order (deterministic whatever the
       // arrival order) and writes D.  Partials are kept in register order, not
@@ -760,7 +776,7 @@ gemm_kernel(GemmParams p) {
       const int tile_mn = cur.mt * tiles_n + cur.nt;
       constexpr int kTileFloats = C::BM * C::BN;
       const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
-          p.ws + (int64_t)tile_mn * p.splits * kTileFloats, 0, p.splits * kTileFloats * 4, kRawBufferFlags);
+          p.ws + (int64_t)tile_mn * splits * kTileFloats, 0, splits * kTileFloats * 4, kRawBufferFlags);
       const int lane_off = ((wave * C::kMfmas) * 64 + lane) * 16;   // bytes, (ms, j) = (0, 0)
 #pragma unroll
       for (int ms = 0; ms < C::MS; ++ms)
@@ -775,7 +791,7 @@ gemm_kernel(GemmParams p) {
       __syncthreads();
       if (threadIdx.x == 0)
         last_flag = __hip_atomic_fetch_add(p.counters + tile_mn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    p.splits - 1;
+                    splits - 1;
       __syncthreads();
       if (last_flag) {
 #pragma unroll
@@ -786,7 +802,7 @@ gemm_kernel(GemmParams p) {
         // add, so one memory round trip serves the whole batch; the adds then
         // run in split order.
         constexpr int kBatch = 32 / (C::kMfmas * 4) > 0 ? 32 / (C::kMfmas * 4) : 1;
-        for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
+        for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
           f32x4 v[kBatch][C::MS][C::NS];
 #pragma unroll
           for (int b = 0; b < kBatch; ++b)
@@ -794,7 +810,7 @@ gemm_kernel(GemmParams p) {
             for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
               for (int j = 0; j < C::NS; ++j)
-                v[b][ms][j] = sp0 + b < p.splits
+                v[b][ms][j] = sp0 + b < splits
                                   ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                   part, lane_off + (ms * C::NS + j) * 1024,
                                                                   (sp0 + b) * kTileFloats * 4, kScopeDevice))
@@ -805,7 +821,7 @@ gemm_kernel(GemmParams p) {
             for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
               for (int j = 0; j < C::NS; ++j)
-                if (sp0 + b < p.splits) acc[ms][j] += v[b][ms][j];
+                if (sp0 + b < splits) acc[ms][j] += v[b][ms][j];
         }
         // ready for the next call
         if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile_mn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -871,6 +887,10 @@ hipError_t launch_variant(Variant v, const GemmParams& p, int grid, hipStream_t 
       if constexpr ((Mask >> kDenseSplitK) & 1)
         hipLaunchKernelGGL((gemm_kernel<C, kDenseSplitK>), dim3(grid), block, 0, stream, p);
       break;
+    case kContiguousSplitK:
+      if constexpr ((Mask >> kContiguousSplitK) & 1)
+        hipLaunchKernelGGL((gemm_kernel<C, kContiguousSplitK>), dim3(grid), block, 0, stream, p);
+      break;
   }
   return hipGetLastError();
 }
@@ -881,7 +901,8 @@ hipError_t launch_cfg(Variant v, const GemmParams& p, int grid, hipStream_t stre
                      : launch_variant<C, Mask>(v, p, grid, stream);
 }
 
-constexpr int kAll = (1 << kDense) | (1 << kContiguous) | (1 << kMasked) | (1 << kDenseSplitK);
+constexpr int kAll = (1 << kDense) | (1 << kContiguous) | (1 << kMasked) | (1 << kDenseSplitK) |
+                     (1 << kContiguousSplitK);
 constexpr int kDenseAndSplit = (1 << kDense) | (1 << kDenseSplitK);
 
 }  // namespace

@@ -225,6 +225,28 @@ def test_forced_dense_plan_is_reported_and_checked():
     dg.set_dense_plan(-1)
 
 
+def test_contiguous_workspace_size_follows_the_plan():
+    import moe_fp8_gemm_amd as dg
+    hw = dg.get_num_cus()
+    # G=8 over 66 blocks (the paired plan with 2 leftover blocks): one 128x128
+    # fp32 partial tile per CU plus the 256 KiB counter block
+    assert dg.contiguous_workspace_size(8448, 4096, 7168, 8) == 256 * 1024 + hw * 128 * 128 * 4
+    try:
+        dg.set_contiguous_plan(2)                      # one tile per block: never splits
+        assert dg.contiguous_workspace_size(8448, 4096, 7168, 8) == 0
+        dg.set_contiguous_plan(1)
+        assert dg.contiguous_workspace_size(1024, 520, 256, 4) == 0     # 2 K blocks: too few to split
+        full = dg.contiguous_workspace_size(1024, 520, 2048, 4)
+        assert full > 0
+        dg.set_num_cus(5)                               # the grid width does not change the plan
+        assert dg.contiguous_workspace_size(1024, 520, 2048, 4) == full
+    finally:
+        dg.set_contiguous_plan(0)
+        dg.set_num_cus(0)
+    for bad in [(1000, 64, 256, 2), (1024, 64, 200, 2), (1024, 64, 256, 0), (0, 64, 256, 2)]:
+        assert dg.contiguous_workspace_size(*bad) == 0
+
+
 # ------------------------------------------------------------------ binding: scale shapes
 
 def test_binding_rejects_scale_tensors_of_the_wrong_shape():

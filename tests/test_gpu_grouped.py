@@ -39,10 +39,13 @@ def _contig_host(num_groups, tokens, n, k, seed, ue8m0=False):
     return w, qa, sa, qb, sb
 
 
-def _gpu_contig(qa, sa, qb, sb, m_indices):
+def _gpu_contig(qa, sa, qb, sb, m_indices, workspace="auto", packed=False):
     d = sentinel_like((qa.shape[0], qb.shape[1]))
-    dg.m_grouped_fp8_gemm_nt_contiguous((upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb)), d,
-                                        upload(m_indices))
+    a_s, b_s = upload(sa), upload(sb)
+    if packed:
+        a_s, b_s = dg.pack_ue8m0(a_s), dg.pack_ue8m0(b_s)
+    dg.m_grouped_fp8_gemm_nt_contiguous((upload_codes(qa), a_s), (upload_codes(qb), b_s), d,
+                                        upload(m_indices), workspace=workspace)
     torch.cuda.synchronize()
     return bits(d)
 
@@ -58,8 +61,9 @@ def test_contiguous_parity_small(groups, tokens, n, k):
 
 
 def test_contiguous_equals_dense_on_each_group_and_groups_are_independent():
+    # without a workspace no K is split, so every row is computed as the dense GEMM computes it
     w, qa, sa, qb, sb = _contig_host(3, 500, 392, 512, seed=11)
-    got = _gpu_contig(qa, sa, qb, sb, w.m_indices)
+    got = _gpu_contig(qa, sa, qb, sb, w.m_indices, workspace=None)
     for g in range(3):
         rows = np.nonzero(w.m_indices == g)[0]
         d = sentinel_like((rows.size, qb.shape[1]))
@@ -68,7 +72,7 @@ def test_contiguous_equals_dense_on_each_group_and_groups_are_independent():
         assert np.array_equal(bits(d), got[rows]), g
     qb2 = qb.copy()
     qb2[1] ^= 0x80
-    got2 = _gpu_contig(qa, sa, qb2, sb, w.m_indices)
+    got2 = _gpu_contig(qa, sa, qb2, sb, w.m_indices, workspace=None)
     same = w.m_indices != 1
     assert np.array_equal(got2[same], got[same])
 
@@ -225,6 +229,73 @@ def test_contiguous_pair_plan_layouts(name):
             assert np.array_equal(_gpu_contig(qa, sa, qb, sb, m_indices), got)
     finally:
         dg.set_num_cus(0)
+
+
+def _paired_blocks(m_indices):
+    """Blocks the paired plan covers with 256-row tiles: in each run of
+    consecutive blocks of one group (a block's group is that of its first row;
+    padding blocks end a run), blocks pair up from the start of the run."""
+    nb = m_indices.size // 128
+    grp = m_indices[::128]
+    paired = np.zeros(nb, bool)
+    b = 0
+    while b < nb:
+        if grp[b] < 0:
+            b += 1
+            continue
+        e = b
+        while e + 1 < nb and grp[e + 1] == grp[b]:
+            e += 1
+        length = e - b + 1
+        paired[b:b + length // 2 * 2] = True
+        b = e + 1
+    return paired
+
+
+SPLIT_LAYOUTS = {
+    # 3 pairs and 4 leftover blocks over 4 groups, ragged last blocks, a padding block
+    "mixed": [(0, 3, 100), (1, 1, 77), (2, 2, 128), (3, 1, 5), (-1, 1, 0), (1, 3, 128)],
+    # one block per group: everything runs in the second launch
+    "all_leftover": [(0, 1, 128), (1, 1, 64), (2, 1, 1), (3, 1, 128)],
+}
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("name", sorted(SPLIT_LAYOUTS))
+def test_contiguous_split_leftover_blocks(name, packed):
+    """With a workspace, the paired plan's second launch splits K over the CUs
+    its few tiles leave idle (the split is chosen on the device from the
+    number of leftover blocks).  Rows of paired blocks keep the bits of the
+    unsplit call; every row is within the oracle's tolerance; the result is
+    deterministic, independent of the grid width, and (power-of-two scales)
+    the same with packed UE8M0 words as with fp32 words."""
+    m_indices = _segments_layout(SPLIT_LAYOUTS[name])
+    groups, n, k = 4, 520, 2048
+    qa, sa, qb, sb = _random_problem(m_indices.size, groups, n, k, seed=m_indices.size)
+    if packed:
+        sa, sb = np.exp2(np.round(np.log2(sa))).astype(np.float32), np.exp2(np.round(np.log2(sb))).astype(np.float32)
+    with _contig_plan(1):
+        assert dg.contiguous_workspace_size(m_indices.size, n, k, groups) > 0, "no split planned"
+        print(f"contiguous split {name} packed={packed}", flush=True)
+        split = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)
+        again = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)
+        unsplit = _gpu_contig(qa, sa, qb, sb, m_indices, workspace=None, packed=packed)
+        try:
+            dg.set_num_cus(3)
+            narrow = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)
+        finally:
+            dg.set_num_cus(0)
+        if packed:
+            fp32_words = _gpu_contig(qa, sa, qb, sb, m_indices)
+            assert np.array_equal(split, fp32_words)
+    assert np.array_equal(split, again) and np.array_equal(split, narrow)
+    pad = m_indices < 0
+    assert np.all(split[pad] == SENTINEL), "padding rows written"
+    paired_rows = np.repeat(_paired_blocks(m_indices), 128)
+    assert np.array_equal(split[paired_rows], unsplit[paired_rows])
+    want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, m_indices)
+    assert_gemm_close(split[~pad], want[~pad], f"split {name}")
+    assert_gemm_close(unsplit[~pad], want[~pad], f"unsplit {name}")
 
 
 @pytest.mark.parametrize("nblocks", [2048, 2049])

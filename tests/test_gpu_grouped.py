@@ -298,6 +298,56 @@ def test_contiguous_split_leftover_blocks(name, packed):
     assert_gemm_close(unsplit[~pad], want[~pad], f"unsplit {name}")
 
 
+def test_contiguous_split_plan_graph_replays_with_new_routing():
+    """The paired plan with split leftover blocks, captured once as a HIP graph
+    and replayed with routings of the same 8 blocks whose leftover-block count
+    differs (2, 4, 0, 1), so that the split the kernel picks on the device
+    changes between replays.  Every replay must equal an eager call bit for bit
+    and match the oracle; the workspace's counters must come back zero."""
+    groups, n, k = 4, 520, 2048
+    routings = [[(0, 3, 128), (1, 2, 90), (2, 1, 128), (3, 2, 7)],
+                [(0, 1, 128), (1, 1, 64), (2, 1, 128), (3, 5, 100)],
+                [(3, 2, 128), (2, 2, 128), (1, 2, 1), (0, 2, 128)],
+                [(1, 6, 128), (0, 1, 33), (2, 1, 128)]]
+    layouts = [_segments_layout(r) for r in routings]
+    m_total = layouts[0].size
+    assert all(l.size == m_total for l in layouts)
+    qa, sa, qb, sb = _random_problem(m_total, groups, n, k, seed=77)
+    a = (upload_codes(qa), upload(sa))
+    b = (upload_codes(qb), upload(sb))
+    mi = upload(layouts[0])
+    d = sentinel_like((m_total, n))
+    with _contig_plan(1):
+        need = dg.contiguous_workspace_size(m_total, n, k, groups)
+        assert need > 0
+        ws = torch.zeros(need, dtype=torch.uint8, device=device())
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi, workspace=ws)     # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dg.m_grouped_fp8_gemm_nt_contiguous(a, b, d, mi, workspace=ws)
+        for rep, layout in enumerate(layouts[1:] + layouts[:1]):
+            print(f"split-plan graph replay {rep}: {int((~_paired_blocks(layout) & (layout[::128] >= 0)).sum())} "
+                  "leftover blocks", flush=True)
+            mi.copy_(torch.from_numpy(layout))
+            d.view(torch.int16).fill_(SENTINEL)                    # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got = bits(d)
+            assert int(ws[:256 * 1024].view(torch.int32).abs().sum().item()) == 0, "counters not left zero"
+            eager = _gpu_contig(qa, sa, qb, sb, layout, workspace=ws)
+            assert np.array_equal(got, eager), rep
+            pad = layout < 0
+            assert np.all(got[pad] == SENTINEL)
+            want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, layout)
+            assert_gemm_close(got[~pad], want[~pad], f"split-plan replay {rep}")
+
+
 @pytest.mark.parametrize("nblocks", [2048, 2049])
 def test_contiguous_pair_plan_largest_layout(nblocks):
     """2048 blocks is the largest layout the paired plan takes (its tile list

@@ -127,6 +127,22 @@ def test_contiguous_validation(lib):
     assert call(m_total=65536, k=65536, ld=65536) == 2   # A row offsets beyond 32 bits
 
 
+def test_contiguous_workspace_entry_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ws
+    i = ctypes.c_int64
+
+    def call(ws, ws_bytes, m_total=256, groups=2, k=512, ld=512):
+        kb = ld // 128
+        return f(P, i(ld), P, i(kb), i(1), P, i(ld), i(256 * ld), P, i(kb), i(1), i(2 * kb), P, i(256),
+                 P, i(m_total), i(256), i(k), ctypes.c_int(groups), ws, ctypes.c_size_t(ws_bytes), None)
+
+    assert call(ctypes.c_void_p(0x10008), 1 << 24) == 2      # workspace not 16-byte aligned
+    assert call(P, 1 << 24, m_total=200) == 3                 # MISALIGNED_LAYOUT, as without workspace
+    assert call(P, 1 << 24, groups=0) == 1
+    assert call(P, 1 << 24, k=500) == 2
+    assert call(P, 1 << 24, m_total=0) == 0                   # empty problem: success, no launch
+
+
 def test_masked_validation(lib):
     f = lib.dg_m_grouped_fp8_gemm_nt_masked
     i = ctypes.c_int64

@@ -275,11 +275,15 @@ def test_contiguous_split_leftover_blocks(name, packed):
     if packed:
         sa, sb = np.exp2(np.round(np.log2(sa))).astype(np.float32), np.exp2(np.round(np.log2(sb))).astype(np.float32)
     with _contig_plan(1):
-        assert dg.contiguous_workspace_size(m_indices.size, n, k, groups) > 0, "no split planned"
+        need = dg.contiguous_workspace_size(m_indices.size, n, k, groups)
+        assert need > 0, "no split planned"
         print(f"contiguous split {name} packed={packed}", flush=True)
         split = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)
         again = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)
         unsplit = _gpu_contig(qa, sa, qb, sb, m_indices, workspace=None, packed=packed)
+        # a workspace one byte short of the plan's need: the call runs unsplit
+        short = torch.zeros(need - 1, dtype=torch.uint8, device=device())
+        assert np.array_equal(_gpu_contig(qa, sa, qb, sb, m_indices, workspace=short, packed=packed), unsplit)
         try:
             dg.set_num_cus(3)
             narrow = _gpu_contig(qa, sa, qb, sb, m_indices, packed=packed)

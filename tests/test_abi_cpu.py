@@ -21,7 +21,7 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libdgfp8.so not built (run __graft_entry__.build())")
+        pytest.fail("libdgfp8.so not built (run python moe_fp8_gemm_amd/build.py)")
     return ctypes.CDLL(LIB)
 
 

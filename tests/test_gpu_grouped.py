@@ -495,6 +495,28 @@ def test_masked_parity_small_with_edge_counts():
             assert_gemm_close(got[g, :c], want[g, :c], f"masked group {g}")
 
 
+def test_masked_largest_group_count():
+    # 1024 groups, the most the device-side prefix over masked_m holds: counts
+    # spread over every lane's share of the prefix, with empty groups, full
+    # groups, and values the kernel clamps (negative, above max_m); both tile
+    # heights give the same bits, and every group matches the oracle.
+    groups, max_m, n, k = 1024, 64, 64, 128
+    rng = np.random.default_rng(31)
+    mm = rng.integers(0, max_m + 1, size=groups)
+    mm[rng.random(groups) < 0.1] = 0
+    mm[rng.random(groups) < 0.1] = max_m
+    mm[5], mm[700], mm[1023] = -3, max_m + 40, 1
+    qa, sa, qb, sb, masked_m = _masked_host(groups, max_m, n, k, seed=32, masked_m=mm)
+    print(f"masked {groups} groups, {int(np.clip(mm, 0, max_m).sum())} rows", flush=True)
+    got = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=16)
+    assert np.array_equal(_gpu_masked(qa, sa, qb, sb, masked_m, expected_m=128), got)
+    want = ogemm.m_grouped_masked(qa, sa, qb, sb, masked_m)
+    rows = np.clip(mm, 0, max_m)
+    valid = np.arange(max_m)[None, :] < rows[:, None]
+    assert np.all(got[~valid] == SENTINEL), "rows beyond masked_m written"
+    assert_gemm_close(got[valid], want[valid], "1024 masked groups")
+
+
 @pytest.mark.parametrize("max_m,counts", [(130, [130, 3, 0, 77]), (100, [100, 65, 64, 1])])
 def test_masked_expected_m_is_only_a_hint(max_m, counts):
     """The hint picks the tile (64-row decode tiles up to 64, else 256- or

@@ -59,6 +59,22 @@ def test_dense_parity_small(m, n, k):
     assert_gemm_close(got, ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(64, 264, 65536), (300, 136, 32768)])
+def test_dense_long_k(m, n, k):
+    # 512 and 256 K blocks: the per-block mantissa rescale runs hundreds of
+    # times per accumulator, over the split-K plan the planner picks (M = 64)
+    # and over whole tiles (M = 300), and with no workspace (no split)
+    print(f"dense long K {m}x{n}x{k} plan {dg.tile_config(m, n, k)}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + k)
+    want = ogemm.gemm_nt(qa, sa, qb, sb)
+    assert_gemm_close(_gpu_dense(qa, sa, qb, sb), want, f"{m}x{n}x{k}")
+    a, b = (upload_codes(qa), upload(sa)), (upload_codes(qb), upload(sb))
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d, workspace=None)
+    torch.cuda.synchronize()
+    assert_gemm_close(bits(d), want, f"{m}x{n}x{k} unsplit")
+
+
 def test_config0_workload():
     w = synth.config0()
     qa, sa = quant.per_token_cast(w.a)

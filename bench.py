@@ -179,6 +179,7 @@ def pipelined_cold_us(dg, a, b, d, min_bytes_total=600 << 20, reps=5):
 def bench_extras(dg, dev, reps):
     out = {}
     flush = Flusher(dev)
+    traffic = counted_traffic()
     # --- contiguous G=8 (prefill) and masked G=16 (decode)
     for idx, (n, k) in enumerate(synth.GROUPED_NK):
         counts, m_indices = synth.config2_routing(idx)
@@ -202,7 +203,8 @@ def bench_extras(dg, dev, reps):
         out[f"contiguous_G8_{n}x{k}"] = {
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
             "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "m_total": m_total,
-            "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil}
+            "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil,
+            "hbm_gbs_counted": counted_gbs(traffic, f"contiguous_G8_{n}x{k}", ms * 1e3)}
         del qa, sa, qb, sb, d
 
         masked_m = synth.config3_masked_m(idx)
@@ -226,7 +228,8 @@ def bench_extras(dg, dev, reps):
         ceil = ceiling_tflops(useful, min_bytes(int(masked_m.sum()), n, k, 16))
         out[f"masked_G16_{n}x{k}"] = {
             "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS,
-            "b_read_gbs": b_bytes / ms / 1e6, "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil}
+            "b_read_gbs": b_bytes / ms / 1e6, "ceiling_tflops": ceil, "pct_of_ceiling": 100 * useful / ms / 1e9 / ceil,
+            "hbm_gbs_counted": counted_gbs(traffic, f"masked_G16_{n}x{k}", ms * 1e3)}
         # decode shape on the same operands: 0..32 rows per group, run on the
         # 64-row decode tiles (hint 16) and on the 256-row tiles (hint 128)
         mm_dec = torch.from_numpy(synth.masked_counts(16, 32, seed + 500)).to(dev)
@@ -234,7 +237,10 @@ def bench_extras(dg, dev, reps):
         ms_big = event_time_ms(lambda: dg.m_grouped_fp8_gemm_nt_masked((qa, sa), (qb, sb), d, mm_dec, 128), reps, flush)
         out[f"masked_decode_G16_{n}x{k}"] = {
             "rows": int(mm_dec.sum().item()), "us_64row_tiles": ms_dec * 1e3, "us_256row_tiles": ms_big * 1e3,
-            "b_read_gbs_64row_tiles": b_bytes / ms_dec / 1e6, "b_read_gbs_256row_tiles": b_bytes / ms_big / 1e6}
+            "b_read_gbs_64row_tiles": b_bytes / ms_dec / 1e6, "b_read_gbs_256row_tiles": b_bytes / ms_big / 1e6,
+            "hbm_gbs_counted_64row_tiles": counted_gbs(traffic, f"masked_decode_G16_{n}x{k}_64row_tiles", ms_dec * 1e3),
+            "hbm_gbs_counted_256row_tiles": counted_gbs(traffic, f"masked_decode_G16_{n}x{k}_256row_tiles",
+                                                        ms_big * 1e3)}
         del qa, sa, qb, sb, d
     # --- dense M=4096 shapes with power-of-two scales: fp32 scale words vs packed UE8M0 words
     shapes4k = [s for s in synth.config1_shapes() if s[0] == 4096]
@@ -289,7 +295,10 @@ def bench_extras(dg, dev, reps):
         "us": ms * 1e3, "tflops_useful": useful / ms / 1e9, "tflops_padded": 2.0 * m_total * n * k / ms / 1e9,
         "pct_fp8_peak": 100 * useful / ms / 1e9 / FP8_PEAK_TFLOPS, "b_read_gbs": 256 * n * k / ms / 1e6,
         "m_total": m_total, "us_packed_ue8m0_scales": ms_p * 1e3,
-        "tflops_useful_packed_ue8m0": useful / ms_p / 1e9}
+        "tflops_useful_packed_ue8m0": useful / ms_p / 1e9,
+        "hbm_gbs_counted": counted_gbs(traffic, "contiguous_zipf_G256_4096x7168_ue8m0", ms * 1e3),
+        "hbm_gbs_counted_packed_ue8m0": counted_gbs(traffic, "contiguous_zipf_G256_4096x7168_ue8m0_packed",
+                                                    ms_p * 1e3)}
     del pa, pb
     del qa, sa, qb, sb, d
     # --- per-token cast of the bf16 activation
@@ -442,6 +451,36 @@ def measured_profile(cfg, shapes):
     return kv
 
 
+TRAFFIC_ROWS_FILE = os.path.join(ROOT, "profiles", "traffic_hbm_bound.txt")
+
+
+def counted_traffic():
+    """{row: calibrated HBM bytes per call} from the committed counter summary of
+    the HBM-bound rows (FETCH_SIZE / calibration + WRITE_SIZE / calibration, in
+    bytes); empty when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_ROWS_FILE):
+        return {}
+    kv = {}
+    for line in open(TRAFFIC_ROWS_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.pop("kernel_source_sha256", None) != gemm_source_sha256():
+        return {}
+    fc, wc = float(kv.pop("fetch_calibration")), float(kv.pop("write_calibration"))
+    out = {}
+    for row, val in kv.items():
+        fetch, write = (float(x) for x in val.split())
+        out[row] = (fetch / fc + write / wc) * 1024
+    return out
+
+
+def counted_gbs(traffic, row, us):
+    """Counted HBM GB/s of one call of `row` that took `us` microseconds (None
+    without a valid counter figure)."""
+    return round(traffic[row] / (us * 1e-6) / 1e9, 1) if row in traffic and us > 0 else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -561,6 +600,7 @@ def main():
                           "tflops": flops[i] / (mean_ms[i] * 1e-3) / 1e12})
     log("cold-cache per-shape times")
     flush = Flusher(dev)
+    traffic = counted_traffic()
     for i, (a, b, d) in enumerate(probs):
         ms = event_time_ms(lambda: dg.fp8_gemm_nt(a, b, d), 10, flush)
         per_shape[i]["us_cold"] = ms * 1e3
@@ -570,6 +610,7 @@ def main():
         per_shape[i]["ceiling_tflops"] = ceil
         per_shape[i]["pct_of_ceiling_cold"] = 100 * per_shape[i]["tflops_cold"] / ceil
         if shapes[i][0] <= 128:
+            per_shape[i]["hbm_gbs_counted_cold"] = counted_gbs(traffic, "%dx%dx%d" % shapes[i], ms * 1e3)
             # Back-to-back launches over enough distinct operand copies (> 512 MB
             # in all) that every launch still reads its operands from HBM: the
             # per-launch event overhead is paid once per batch, not per launch.

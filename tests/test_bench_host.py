@@ -1,4 +1,5 @@
-"""Host-side arithmetic of bench.py's roofline ceilings (no GPU).
+"""Host-side arithmetic of bench.py's roofline ceilings and counted-traffic
+fields (no GPU).
 
 Expected values are worked out by hand from the workload shapes: bytes = A
 (M*K) + B (N*K) + fp32 scales (M*K/128 and ceil(N/128)*K/128 words) + bf16 D
@@ -28,3 +29,23 @@ def test_ceilings():
     assert 975 < c < 976.5
     # MFMA-bound: the 4096 x 7168 x 16384 shape is capped at the FP8 peak
     assert bench.ceiling_tflops(2.0 * 4096 * 7168 * 16384, bench.min_bytes(4096, 7168, 16384)) == 5000.0
+
+
+def test_counted_traffic_rows():
+    # 64 x 2112 x 7168: FETCH_SIZE 11159 KiB (reads 0.5x of the true bytes) and
+    # WRITE_SIZE 3968 KiB per call -> (22318 + 3968) KiB = 26.92 MB
+    t = bench.counted_traffic()
+    if not t:   # kernel sources changed since the counters were taken
+        return
+    assert math.isclose(t["64x2112x7168"], (11159 / 0.5 + 3968) * 1024, rel_tol=1e-12)
+    rows = {"%dx%dx%d" % (m, n, k) for m in (64, 128)
+            for (n, k) in ((2112, 7168), (24576, 1536), (7168, 16384), (4096, 7168), (7168, 2048))}
+    assert rows <= set(t)
+    # 26.92 MB in 10 us -> 2691.6 GB/s
+    assert bench.counted_gbs(t, "64x2112x7168", 10.0) == round(26.916864e6 / 10e-6 / 1e9, 1)
+    assert bench.counted_gbs(t, "no such row", 10.0) is None
+
+
+def test_counted_traffic_ignored_after_a_kernel_change(monkeypatch):
+    monkeypatch.setattr(bench, "gemm_source_sha256", lambda: "0" * 64)
+    assert bench.counted_traffic() == {}

@@ -6,7 +6,8 @@ Two split-K calls in a row on the library's static scratch, the second one on
 a smaller problem, then an unsplit one; each must give the workspace entry
 point's bits (same plan, same kernels) and pass the oracle tolerance.  A
 problem whose split plan needs more scratch than the static maximum is
-rejected before anything is launched.
+rejected before anything is launched.  Split-K calls captured in a HIP graph
+replay with the eager calls' bits.
 """
 import ctypes
 
@@ -90,3 +91,47 @@ def test_noalloc_rejects_plans_beyond_the_static_scratch():
         dg.fp8_gemm_nt_noalloc((a, sa), (b, sb), d)
     torch.cuda.synchronize()
     assert bool((d.view(torch.int16) == 0x7FC1).all()), "output touched"
+
+
+def test_noalloc_under_graph_capture():
+    """What the entry point is for: split-K calls on the static scratch recorded
+    in a HIP graph (no allocation may happen while capturing), replayed three
+    times with eager calls on the same scratch in between.  Every replay must
+    give the bits of the eager calls."""
+    shapes = [(128, 7168, 2048), (64, 2112, 7168)]
+    probs = []
+    for i, (m, n, k) in enumerate(shapes):
+        assert dg.tile_config(m, n, k)[2] > 1, "shape no longer splits K"
+        qa, sa, qb, sb = _problem(m, n, k, seed=90 + i)
+        probs.append((upload_codes(qa), upload(sa), upload_codes(qb), upload(sb)))
+    want = []
+    for a, sa_t, b, sb_t in probs:
+        d = sentinel_like((a.shape[0], b.shape[0]))
+        dg.fp8_gemm_nt_noalloc((a, sa_t), (b, sb_t), d)
+        want.append(d)
+    torch.cuda.synchronize()
+    want_bits = [bits(d) for d in want]
+    outs = [sentinel_like(d.shape) for d in want]
+    side = sentinel_like(want[0].shape)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    print("no-alloc: capturing two split-K calls", flush=True)
+    with torch.cuda.graph(g, stream=s):
+        for (a, sa_t, b, sb_t), d in zip(probs, outs):
+            dg.fp8_gemm_nt_noalloc((a, sa_t), (b, sb_t), d)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for d in outs:
+            d.view(torch.int16).fill_(0x7FC1)
+        print(f"no-alloc: replay {r}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for d, wb, (m, n, k) in zip(outs, want_bits, shapes):
+            assert np.array_equal(bits(d), wb), f"replay {r}, {m}x{n}x{k}: differs from the eager call"
+        # an eager call between replays shares the scratch (its counters must come back zero)
+        a, sa_t, b, sb_t = probs[0]
+        dg.fp8_gemm_nt_noalloc((a, sa_t), (b, sb_t), side)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(side), want_bits[0])
+    del g

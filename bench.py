@@ -38,6 +38,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -587,6 +588,11 @@ def main():
     dom_time = dom_total_ms / (args.steps * len(big))
     dom_flops = float(np.mean([flops[i] for i in big]))
     achieved = dom_flops / (dom_time * 1e-3) / 1e12
+    # Operand bytes the dominant instance stages from L2 into LDS per launch:
+    # every tile copies its A rows and B rows of each 128-wide K block once.
+    bm, bn = dom_cfg[0], dom_cfg[1]
+    staged = float(np.mean([math.ceil(shapes[i][0] / bm) * math.ceil(shapes[i][1] / bn) * (shapes[i][2] // 128)
+                            * (bm + bn) * 128 for i in big]))
     if args.calib_copy:
         src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -649,6 +655,8 @@ def main():
                                                             "" if dom_cfg[2] == 1 else ", split-K %d" % dom_cfg[2]),
                      "shapes": ["%dx%dx%d" % shapes[i] for i in big],
                      "avg_launch_us": round(dom_time * 1e3, 2), "flops_per_launch": dom_flops,
+                     "staged_bytes_per_launch": int(staged),
+                     "staged_gbs_per_cu": round(staged / (dom_time * 1e-3) / 1e9 / 256, 1),
                      "sclk_ghz_profiled": sclk,
                      "peak_at_profiled_sclk": round(peak_at_sclk, 1) if sclk else None,
                      "frac_at_profiled_sclk": round(achieved / peak_at_sclk, 4) if sclk else None},

@@ -496,8 +496,8 @@ def main():
                     help="profiling aid: time only this M,N,K of the workload (e.g. 4096,4096,7168)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this library runs on one GPU; multi-GPU (expert-parallel) runs are not part of "
-              "this build -- use --gpus 1", file=sys.stderr)
+        print("bench.py: this library runs on one GPU; multi-GPU (expert-parallel) runs are not "
+              "implemented -- use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import moe_fp8_gemm_amd as dg
 

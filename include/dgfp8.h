@@ -43,6 +43,12 @@
  * Alignment contract: K % 128 == 0; lda, ldb and the A/B base addresses are
  * multiples of 16 bytes; N % 8 == 0, ldd % 8 == 0 and D is 16-byte aligned.
  * Violations return DG_ERROR_NOT_SUPPORTED.
+ *
+ * Size contract: one group's A rows and B rows are addressed with 32-bit byte
+ * offsets (rows x leading dimension < 2^32), and no size, leading dimension,
+ * scale stride or group stride may exceed 2^40; larger values return
+ * DG_ERROR_NOT_SUPPORTED before anything is launched (the casts and the
+ * scale packing apply the 2^40 bound too).
  */
 #ifndef DGFP8_H_
 #define DGFP8_H_

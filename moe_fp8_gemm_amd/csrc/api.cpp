@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <initializer_list>
 
 #include "dgfp8_internal.h"
 
@@ -42,6 +43,16 @@ int device_cus() { return g_num_cus_override > 0 ? g_num_cus_override : hw_cus()
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Strides (elements) and sizes no real buffer comes near: 2^40.  Rejecting
+// larger ones keeps every product of two of them inside int64 (in this file
+// and in the kernels' 64-bit offset arithmetic).
+constexpr int64_t kMaxStride = (int64_t)1 << 40;
+bool strides_ok(std::initializer_list<int64_t> v) {
+  for (int64_t x : v)
+    if (x > kMaxStride) return false;
+  return true;
+}
+
 // Checks shared by the three GEMM variants.
 dg_status check_common(const void* a, int64_t lda, const void* sfa, int64_t sfa_sm, int64_t sfa_sk,
                        const void* b, int64_t ldb, const void* sfb, int64_t sfb_sn, int64_t sfb_sk,
@@ -50,6 +61,7 @@ dg_status check_common(const void* a, int64_t lda, const void* sfa, int64_t sfa_
   if (n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
   if (sfa_sm < 0 || sfa_sk < 0 || sfb_sn < 0 || sfb_sk < 0) return DG_ERROR_INVALID_VALUE;
   if (lda < k || ldb < k || ldd < n) return DG_ERROR_INVALID_VALUE;
+  if (!strides_ok({lda, ldb, ldd, sfa_sm, sfa_sk, sfb_sn, sfb_sk, n, k})) return DG_ERROR_NOT_SUPPORTED;
   if (k == 0 || k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
   if (n % 8 != 0 || ldd % 8 != 0) return DG_ERROR_NOT_SUPPORTED;
   if (lda % 16 != 0 || ldb % 16 != 0) return DG_ERROR_NOT_SUPPORTED;
@@ -285,9 +297,16 @@ dg_status launch(GemmInstance inst, Variant v, const GemmParams& p, int64_t tile
 
 // The kernels address one group's operand rows with 32-bit byte offsets.
 bool offsets_fit(int64_t rows_a, int64_t lda, int64_t n, int64_t ldb) {
+  // rows * ld <= 2^32 - 1, written so that no product can overflow
   const int64_t lim = (int64_t)UINT32_MAX;
-  return (rows_a - 1) * lda + lda <= lim && (n - 1) * ldb + ldb <= lim;
+  return lda > 0 && ldb > 0 && rows_a <= lim / lda && n <= lim / ldb;
 }
+
+// Sizes the planner's integer arithmetic is written for: every product it
+// forms stays far below 2^63.  Larger problems cannot pass offsets_fit either,
+// so the size and plan queries report them as never split / not supported.
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+bool dims_ok(int64_t m, int64_t n, int64_t k) { return m <= kMaxDim && n <= kMaxDim && k <= kMaxDim; }
 
 }  // namespace
 }  // namespace dgfp8
@@ -324,7 +343,7 @@ DG_EXPORT dg_status dg_set_dense_plan(int instance, int splits) {
 }
 
 DG_EXPORT size_t dg_fp8_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {
-  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || !dims_ok(m, n, k)) return 0;
   return (size_t)plan_workspace_bytes(plan_dense(m, n, k, hw_cus(), true));
 }
 
@@ -332,7 +351,7 @@ DG_EXPORT dg_status dg_fp8_gemm_nt_tile_config(int64_t m, int64_t n, int64_t k, 
                                                int* block_n, int* splits) {
   if (!block_m || !block_n || !splits) return DG_ERROR_INVALID_VALUE;
   if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
-  if (k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (k % 128 != 0 || !dims_ok(m, n, k)) return DG_ERROR_NOT_SUPPORTED;
   DensePlan plan = plan_dense(m, n, k, hw_cus(), ws_bytes > 0);
   if ((int64_t)ws_bytes < plan_workspace_bytes(plan)) plan = plan_dense(m, n, k, hw_cus(), false);
   const InstanceInfo info = instance_info(plan.inst);
@@ -463,6 +482,7 @@ dg_status grouped_contiguous(const void* a, int64_t lda, const void* sfa, int64_
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
   if (st != DG_SUCCESS) return st;
   if (b_group_stride % 16 != 0 || !aligned(m_indices, 4)) return DG_ERROR_NOT_SUPPORTED;
+  if (!strides_ok({b_group_stride, sfb_group_stride, m_total})) return DG_ERROR_NOT_SUPPORTED;
   if (!offsets_fit(m_total, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   if (ws && !aligned(ws, 16)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
@@ -554,7 +574,7 @@ DG_EXPORT dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
 DG_EXPORT size_t dg_m_grouped_fp8_gemm_nt_contiguous_workspace_size(int64_t m_total, int64_t n, int64_t k,
                                                                     int num_groups) {
   if (m_total <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || num_groups < 1) return 0;
-  if (m_total % kContiguousAlignment != 0) return 0;
+  if (m_total % kContiguousAlignment != 0 || !dims_ok(m_total, n, k)) return 0;
   const ContigDecision dec = decide_contiguous(m_total, n, k, num_groups, (size_t)INT64_MAX);
   if (!dec.split) return 0;
   return (size_t)contig_split(dec.single, m_total / kContiguousAlignment, n, k, num_groups, hw_cus()).ws_bytes;
@@ -599,6 +619,8 @@ dg_status grouped_masked(const void* a, int64_t lda, int64_t a_group_stride, con
   dg_status st = check_common(a, lda, sfa, sfa_sm, sfa_sk, b, ldb, sfb, sfb_sn, sfb_sk, d, ldd, n, k);
   if (st != DG_SUCCESS) return st;
   if (a_group_stride % 16 != 0 || b_group_stride % 16 != 0 || d_group_stride % 8 != 0 || !aligned(masked_m, 4))
+    return DG_ERROR_NOT_SUPPORTED;
+  if (!strides_ok({a_group_stride, sfa_group_stride, b_group_stride, sfb_group_stride, d_group_stride, max_m}))
     return DG_ERROR_NOT_SUPPORTED;
   if (!offsets_fit(max_m, lda, n, ldb)) return DG_ERROR_NOT_SUPPORTED;
   GemmParams p{};
@@ -659,6 +681,7 @@ dg_status cast_checks(const void* x, int64_t ldx, int64_t x_elem, const void* q,
   if (rows == 0 || k == 0) return DG_SUCCESS;
   if (!x || !q || !sf) return DG_ERROR_INVALID_VALUE;
   if (ldx < k || ldq < k) return DG_ERROR_INVALID_VALUE;
+  if (!strides_ok({ldx, ldq, s0, s1, rows, k})) return DG_ERROR_NOT_SUPPORTED;
   if (k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
   if ((ldx * x_elem) % 16 != 0 || ldq % 16 != 0) return DG_ERROR_NOT_SUPPORTED;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return DG_ERROR_NOT_SUPPORTED;
@@ -703,6 +726,7 @@ DG_EXPORT dg_status dg_pack_ue8m0(const float* sf, int64_t sf_s0, int64_t sf_s1,
   if (rows < 0 || kblocks < 0 || sf_s0 < 0 || sf_s1 < 0 || out_s0 < 0 || out_s1 < 0) return DG_ERROR_INVALID_VALUE;
   if (rows == 0 || kblocks == 0) return DG_SUCCESS;
   if (!sf || !out) return DG_ERROR_INVALID_VALUE;
+  if (!strides_ok({sf_s0, sf_s1, out_s0, out_s1, rows, kblocks})) return DG_ERROR_NOT_SUPPORTED;
   if (!aligned(sf, 4) || !aligned(out, 4)) return DG_ERROR_NOT_SUPPORTED;
   PackParams p{sf, sf_s0, sf_s1, out, out_s0, out_s1, rows, kblocks};
   return launch_pack_ue8m0(p, device_cus(), static_cast<hipStream_t>(stream)) == hipSuccess ? DG_SUCCESS

@@ -315,3 +315,32 @@ def test_build_resource_report_parser_and_no_scratch():
     if os.path.exists(report):
         rows = [l.split() for l in open(report).read().splitlines()[1:] if l.strip()]
         assert rows and all(r[3] == "0" and r[4] == "0" for r in rows), "a kernel uses scratch or spills VGPRs"
+
+
+def test_absurd_sizes_and_strides_are_rejected_without_overflow(lib):
+    # sizes whose products would overflow 64-bit arithmetic come back as
+    # NOT_SUPPORTED (never a wrapped-around pass of the 32-bit offset check)
+    big = 1 << 62
+    assert _gemm(lib, m=big) == 2
+    assert _gemm(lib, m=1 << 33) == 2
+    assert _gemm(lib, ldd=big, n=256) == 2
+    assert _gemm(lib, sfa_sm=big) == 2
+    assert _gemm(lib, lda=big, k=512) == 2
+    i = ctypes.c_int64
+    size = lib.dg_fp8_gemm_nt_workspace_size
+    size.restype = ctypes.c_size_t
+    size.argtypes = [i, i, i]
+    assert size(big, big, 128) == 0
+    cfg = lib.dg_fp8_gemm_nt_tile_config
+    bm, bn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert cfg(i(big), i(big), i(128), ctypes.c_size_t(0), ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(sp)) == 2
+    f = lib.dg_per_token_cast_fp8
+    assert f(P, i(big), P, i(512), P, i(4), i(1), i(8), i(512), 0, None) == 2     # ldx beyond 2^40
+    assert f(P, i(512), P, i(512), P, i(4), i(1), i(big), i(512), 0, None) == 2   # rows beyond 2^40
+    g = lib.dg_per_block_cast_fp8
+    assert g(P, i(1 << 41), P, i(1 << 41), P, i(4), i(1), i(1 << 41), i(1 << 41), 0, None) == 2
+    pack = lib.dg_pack_ue8m0
+    assert pack(P, i(big), i(1), P, i(1), i(1), i(8), i(8), None) == 2
+    m = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert m(P, i(512), i(big), P, i(4), i(1), i(1024), P, i(512), i(256 * 512), P, i(4), i(1),
+             i(8), P, i(256), i(256 * 256), P, ctypes.c_int(4), i(256), i(256), i(512), i(128), None) == 2

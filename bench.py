@@ -614,6 +614,7 @@ def main():
         per_shape[i]["pct_fp8_peak_cold"] = 100 * per_shape[i]["tflops_cold"] / FP8_PEAK_TFLOPS
         ceil = ceiling_tflops(flops[i], min_bytes(*shapes[i]))
         per_shape[i]["ceiling_tflops"] = ceil
+        per_shape[i]["ceiling_us"] = flops[i] / (ceil * 1e12) * 1e6
         per_shape[i]["pct_of_ceiling_cold"] = 100 * per_shape[i]["tflops_cold"] / ceil
         if shapes[i][0] <= 128:
             per_shape[i]["hbm_gbs_counted_cold"] = counted_gbs(traffic, "%dx%dx%d" % shapes[i], ms * 1e3)

@@ -181,6 +181,29 @@ def bench_extras(dg, dev, reps):
     out = {}
     flush = Flusher(dev)
     traffic = counted_traffic()
+    # --- the small parity-sized problem (128 x 256 x 512): launch latency
+    log("extras: dense 128x256x512")
+    a0, b0, d0 = make_dense(dg, 128, 256, 512, synth.seed_for(0, 0), dev)
+    ms0 = event_time_ms(lambda: dg.fp8_gemm_nt(a0, b0, d0), reps, flush)
+    stream0 = torch.cuda.Stream()
+    stream0.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream0):
+        dg.fp8_gemm_nt(a0, b0, d0)
+    torch.cuda.synchronize()
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g0, stream=stream0):
+        for _ in range(100):
+            dg.fp8_gemm_nt(a0, b0, d0)
+    g0.replay()
+    torch.cuda.synchronize()
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    g0.replay()
+    e0.record()
+    torch.cuda.synchronize()
+    out["dense_128x256x512"] = {"us_cold": ms0 * 1e3, "us_back_to_back_graph": s0.elapsed_time(e0) * 1e3 / 100,
+                                "gflop": 2.0 * 128 * 256 * 512 / 1e9}
+    del g0, a0, b0, d0
     # --- contiguous G=8 (prefill) and masked G=16 (decode)
     for idx, (n, k) in enumerate(synth.GROUPED_NK):
         counts, m_indices = synth.config2_routing(idx)

@@ -517,6 +517,36 @@ def test_masked_largest_group_count():
     assert_gemm_close(got[valid], want[valid], "1024 masked groups")
 
 
+@pytest.mark.parametrize("expected_m", [16, 128])
+def test_masked_schedule_does_not_change_the_bits(expected_m):
+    """Masked tiles run heaviest group first, with alternate rounds of the
+    persistent loop walking the tile sequence backwards.  Which tile runs where
+    then depends on masked_m: permuting the groups (operands and counts alike),
+    or narrowing the grid so that each workgroup walks many rounds in both
+    directions, must permute or keep the output bits and nothing else.  Counts
+    include ties, empty groups and groups of two 256-row tiles."""
+    mm = np.array([300, 0, 77, 257, 77, 1, 256, 300, 0, 129, 64, 77], np.int32)
+    groups, max_m, n, k = mm.size, 300, 520, 384
+    qa, sa, qb, sb, masked_m = _masked_host(groups, max_m, n, k, seed=24, masked_m=mm)
+    ref = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m)
+    want = ogemm.m_grouped_masked(qa, sa, qb, sb, masked_m)
+    for g, c in enumerate(mm):
+        assert np.all(ref[g, c:] == SENTINEL), f"group {g}: rows beyond masked_m written"
+        if c:
+            assert_gemm_close(ref[g, :c], want[g, :c], f"masked group {g}")
+    perm = np.random.default_rng(25).permutation(groups)
+    got = _gpu_masked(qa[perm], sa[perm], qb[perm], sb[perm], masked_m[perm], expected_m)
+    assert np.array_equal(got, ref[perm]), "group order changed the bits"
+    for cus in (1, 3, 7, 20):
+        try:
+            dg.set_num_cus(cus)
+            print(f"masked schedule: grid of {cus}", flush=True)
+            narrow = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m)
+        finally:
+            dg.set_num_cus(0)
+        assert np.array_equal(narrow, ref), f"grid of {cus} changed the bits"
+
+
 @pytest.mark.parametrize("max_m,counts", [(130, [130, 3, 0, 77]), (100, [100, 65, 64, 1])])
 def test_masked_expected_m_is_only_a_hint(max_m, counts):
     """The hint picks the tile (64-row decode tiles up to 64, else 256- or

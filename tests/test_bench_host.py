@@ -32,17 +32,17 @@ def test_ceilings():
 
 
 def test_counted_traffic_rows():
-    # 64 x 2112 x 7168: FETCH_SIZE 11159 KiB (reads 0.5x of the true bytes) and
-    # WRITE_SIZE 3968 KiB per call -> (22318 + 3968) KiB = 26.92 MB
+    # 64 x 2112 x 7168: FETCH_SIZE 11161 KiB (reads 0.5x of the true bytes) and
+    # WRITE_SIZE 3968 KiB per call -> (22322 + 3968) KiB = 26.92 MB
     t = bench.counted_traffic()
     if not t:   # kernel sources changed since the counters were taken
         return
-    assert math.isclose(t["64x2112x7168"], (11159 / 0.5 + 3968) * 1024, rel_tol=1e-12)
+    assert math.isclose(t["64x2112x7168"], (11161 / 0.5 + 3968) * 1024, rel_tol=1e-12)
     rows = {"%dx%dx%d" % (m, n, k) for m in (64, 128)
             for (n, k) in ((2112, 7168), (24576, 1536), (7168, 16384), (4096, 7168), (7168, 2048))}
     assert rows <= set(t)
-    # 26.92 MB in 10 us -> 2691.6 GB/s
-    assert bench.counted_gbs(t, "64x2112x7168", 10.0) == round(26.916864e6 / 10e-6 / 1e9, 1)
+    # 26.92 MB in 10 us -> 2692.1 GB/s
+    assert bench.counted_gbs(t, "64x2112x7168", 10.0) == round(26.920960e6 / 10e-6 / 1e9, 1)
     assert bench.counted_gbs(t, "no such row", 10.0) is None
 
 

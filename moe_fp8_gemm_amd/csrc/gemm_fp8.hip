@@ -487,50 +487,25 @@ gemm_kernel(GemmParams p) {
   constexpr bool kSplit = V == kDenseSplitK || V == kContiguousSplitK;
   constexpr bool kContig = V == kContiguous || V == kContiguousSplitK;
   __shared__ int masked_prefix[V == kMasked ? kMaxMaskedGroups + 1 : 1];
-  __shared__ int16_t masked_order[V == kMasked ? kMaxMaskedGroups : 1];
   int tiles_m = 0, num_tiles = 0;
   // K split of a split variant: units (tile, split) with kb_per_split K blocks each
   int splits = kSplit ? p.splits : 1;
   int kb_per_split = p.kb_per_split;
   if constexpr (V == kMasked) {
-    // Masked groups carry different numbers of rows, so their tiles take
-    // different times.  The tile sequence lists the groups heaviest first
-    // (rows decreasing, ties by group index), and the persistent loop walks
-    // odd rounds backwards, so that a workgroup given one of the heaviest tiles
-    // of a round gets one of the lightest of the next.  Every workgroup derives
-    // the same order from masked_m on the device (graph-safe), and a tile's
-    // arithmetic does not depend on where it runs.
-    //   masked_prefix first holds each group's clamped row count, then the
-    // exclusive prefix of M-tile counts over the sorted positions;
-    // masked_order[position] is the group.
-    const int ng = p.num_groups;
-    for (int g = threadIdx.x; g < ng; g += C::kThreads) {
-      int mm = p.masked_m[g];
-      masked_prefix[g] = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
-    }
-    __syncthreads();
-    for (int g = threadIdx.x; g < ng; g += C::kThreads) {
-      const int mine = masked_prefix[g];
-      int rank = 0;
-      for (int h = 0; h < ng; ++h) {
-        const int o = masked_prefix[h];
-        rank += (o > mine || (o == mine && h < g)) ? 1 : 0;
-      }
-      masked_order[rank] = (int16_t)g;
-    }
-    __syncthreads();
+    // Exclusive prefix of per-group M-tile counts, from masked_m on the device.
     if (wave == 0) {
       constexpr int kPer = kMaxMaskedGroups / 64;
       int cnt[kPer];
       int sum = 0;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int pos = lane * kPer + i;
-        const int mm = pos < ng ? masked_prefix[masked_order[pos]] : 0;
+        const int g = lane * kPer + i;
+        int mm = 0;
+        if (g < p.num_groups) mm = p.masked_m[g];
+        mm = mm < 0 ? 0 : (mm > p.m ? (int)p.m : mm);
         cnt[i] = (mm + C::BM - 1) / C::BM;
         sum += cnt[i];
       }
-      // (every lane's reads above precede its writes below)
       int incl = sum;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -588,15 +563,15 @@ gemm_kernel(GemmParams p) {
       int mt, nt, g = 0, split = 0;
       int64_t m_limit = p.m;   // rows that may be written
       if constexpr (V == kMasked) {
-        // sorted position: largest i with prefix[i] * tiles_n <= tile
+        // group: largest g with prefix[g] * tiles_n <= tile
         int lo = 0, hi = p.num_groups;          // invariant: prefix[lo]*tn <= tile < prefix[hi]*tn
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if (masked_prefix[mid] * tiles_n <= tile) lo = mid; else hi = mid;
         }
-        g = masked_order[lo];
-        const int mtiles_g = masked_prefix[lo + 1] - masked_prefix[lo];
-        const int local = tile - masked_prefix[lo] * tiles_n;
+        g = lo;
+        const int mtiles_g = masked_prefix[g + 1] - masked_prefix[g];
+        const int local = tile - masked_prefix[g] * tiles_n;
         nt = local / mtiles_g;
         mt = local % mtiles_g;
         int mm = p.masked_m[g];
@@ -703,30 +678,11 @@ gemm_kernel(GemmParams p) {
     s.okmask = okm;
     return true;
   };
-  // This workgroup's tile of round r (>= num_tiles: none left).  Dense and
-  // contiguous: tile r * grid + b, skipping contiguous padding blocks along the
-  // same stride.  Masked: the sequence is sorted heaviest first and odd rounds
-  // run backwards over the tiles the round has (see above).
-  const int b0 = remap_for_xcd(blockIdx.x, gridDim.x);
-  auto round_tile = [&](int r, int prev, Tile& s) -> int {
-    if constexpr (V == kMasked) {
-      const int grid = (int)gridDim.x;
-      int t;
-      if ((r & 1) == 0) {
-        t = r * grid + b0;
-      } else {
-        const int end = (r + 1) * grid < num_tiles ? (r + 1) * grid : num_tiles;
-        t = end - 1 - b0;
-        if (t < r * grid) t = num_tiles;
-      }
-      if (t < num_tiles) decode(t, s);
-      return t;
-    } else {
-      int tile = r == 0 ? b0 : prev + (int)gridDim.x;
-      for (; tile < num_tiles; tile += gridDim.x)
-        if (decode(tile, s)) break;
-      return tile;
-    }
+  // First tile at or after `tile` (stride gridDim.x) that is not skipped.
+  auto next_tile = [&](int tile, Tile& s) -> int {
+    for (; tile < num_tiles; tile += gridDim.x)
+      if (decode(tile, s)) break;
+    return tile;
   };
   auto prologue = [&](const Tile& s) { tile_dma<C, V>(s.src, s.kbs, wave, lane); };
 
@@ -764,8 +720,7 @@ gemm_kernel(GemmParams p) {
     }
   };
   Tile cur;
-  int round = 0;
-  int tile = round_tile(0, 0, cur);
+  int tile = next_tile(remap_for_xcd(blockIdx.x, gridDim.x), cur);
   if (tile < num_tiles) prologue(cur);
   while (tile < num_tiles) {
     f32x4 acc[C::MS][C::NS];
@@ -805,7 +760,7 @@ gemm_kernel(GemmParams p) {
         for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
     }
     Tile nxt;
-    const int ntile = round_tile(round + 1, tile, nxt);
+    const int ntile = next_tile(tile + gridDim.x, nxt);
     if (kSplit && splits > 1) {
       // Publish this unit's partial tile, count arrivals; the last unit of the
       // output tile adds all partials in split order (deterministic whatever the
@@ -895,7 +850,6 @@ gemm_kernel(GemmParams p) {
     }
     cur = nxt;
     tile = ntile;
-    ++round;
   }
   // Tail steps re-issue the last K block's DMA into free stages: let them land
   // before this workgroup's LDS can be handed to another one.

@@ -519,12 +519,11 @@ def test_masked_largest_group_count():
 
 @pytest.mark.parametrize("expected_m", [16, 128])
 def test_masked_schedule_does_not_change_the_bits(expected_m):
-    """Masked tiles run heaviest group first, with alternate rounds of the
-    persistent loop walking the tile sequence backwards.  Which tile runs where
-    then depends on masked_m: permuting the groups (operands and counts alike),
-    or narrowing the grid so that each workgroup walks many rounds in both
-    directions, must permute or keep the output bits and nothing else.  Counts
-    include ties, empty groups and groups of two 256-row tiles."""
+    """Which workgroup runs which masked tile depends on the group layout and on
+    the grid width.  Permuting the groups (operands and counts alike), or
+    narrowing the grid so that each workgroup walks many tiles, must permute or
+    keep the output bits and nothing else.  Counts include ties, empty groups
+    and groups of two 256-row tiles."""
     mm = np.array([300, 0, 77, 257, 77, 1, 256, 300, 0, 129, 64, 77], np.int32)
     groups, max_m, n, k = mm.size, 300, 520, 384
     qa, sa, qb, sb, masked_m = _masked_host(groups, max_m, n, k, seed=24, masked_m=mm)

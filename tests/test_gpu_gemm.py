@@ -59,6 +59,44 @@ def test_dense_parity_small(m, n, k):
     assert_gemm_close(got, ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
+def _random_shapes(count, seed, m_lo=1, m_hi=700):
+    """Seeded shapes within the documented contract: M from m_lo to m_hi
+    (log-uniform), N a multiple of 8 up to 2400, K a multiple of 128 up to 5120."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        m = int(np.exp(rng.uniform(np.log(m_lo), np.log(m_hi))))
+        n = 8 * int(rng.integers(1, 301))
+        k = 128 * int(rng.integers(1, 41))
+        out.append((max(m, 1), n, k))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", _random_shapes(16, seed=2024) + _random_shapes(6, seed=2025, m_lo=700, m_hi=3000)
+                         + [(4096, 2880, 640), (3000, 4000, 1024)])   # 256x256 and 192x256 tiles
+def test_dense_random_shapes_padded_strides(m, n, k):
+    """Random shapes under the planner's own plan (split K included), with A and
+    B rows padded past K, D rows padded past N and A's scales in either layout:
+    every element matches the oracle, and no padding byte of D is written."""
+    rng = np.random.default_rng(m * 131 + n * 7 + k)
+    plan = dg.tile_config(m, n, k)
+    print(f"random dense {m}x{n}x{k} plan {plan}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=int(rng.integers(1 << 30)))
+    pad_a, pad_b, pad_d = (16 * int(rng.integers(0, 5)) for _ in range(3))
+    a_buf = torch.zeros((m, k + pad_a), dtype=torch.uint8, device=device())
+    a_buf[:, :k] = torch.from_numpy(qa).to(device())
+    b_buf = torch.zeros((n, k + pad_b), dtype=torch.uint8, device=device())
+    b_buf[:, :k] = torch.from_numpy(qb).to(device())
+    d_buf = sentinel_like((m, n + pad_d))
+    sa_t = upload(np.ascontiguousarray(sa.T)).t() if rng.integers(2) else upload(sa)
+    dg.fp8_gemm_nt((a_buf[:, :k].view(torch.float8_e4m3fn), sa_t), (b_buf[:, :k].view(torch.float8_e4m3fn),
+                                                                    upload(sb)), d_buf[:, :n])
+    torch.cuda.synchronize()
+    got = bits(d_buf)
+    assert np.all(got[:, n:] == 0x7FC1), "padding columns of D were written"
+    assert_gemm_close(got[:, :n], ogemm.gemm_nt(qa, sa, qb, sb), f"random {m}x{n}x{k} plan {plan}")
+
+
 @pytest.mark.parametrize("m,n,k", [(64, 264, 65536), (300, 136, 32768)])
 def test_dense_long_k(m, n, k):
     # 512 and 256 K blocks: the per-block mantissa rescale runs hundreds of

@@ -465,6 +465,69 @@ def test_contiguous_full_size_config4_packed_ue8m0():
 
 # ------------------------------------------------------------------ masked
 
+def _random_contiguous_cases(count, seed):
+    """Seeded grouped layouts: 1-12 groups, 1-2000 tokens routed with Dirichlet
+    expert popularity (empty experts included), N a multiple of 8, K a multiple
+    of 128."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        g = int(rng.integers(1, 13))
+        probs = rng.dirichlet(np.full(g, 0.6)).tolist()
+        cases.append((g, int(rng.integers(1, 2001)), 8 * int(rng.integers(1, 200)), 128 * int(rng.integers(1, 25)),
+                      probs, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_contiguous_cases(8, seed=77))
+def test_contiguous_random_layouts(case):
+    """The cost model's plan (paired 256-row tiles, split-K leftover blocks or
+    one tile per block) on random routings: every routed row matches the oracle
+    and every padding row keeps the sentinel."""
+    groups, tokens, n, k, probs, seed = case
+    w = synth.contiguous(groups, tokens, probs, n, k, seed)
+    print(f"contiguous random G={groups} tokens={tokens} rows={w.m_indices.size} {n}x{k} "
+          f"counts={w.counts.tolist()}", flush=True)
+    qa, sa = quant.per_token_cast(w.a)
+    qb, sb = _quant_groups(w.b)
+    got = _gpu_contig(qa, sa, qb, sb, w.m_indices)
+    pad = w.m_indices < 0
+    assert np.all(got[pad] == SENTINEL), "padding rows were written"
+    if (~pad).any():
+        want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, w.m_indices)
+        assert_gemm_close(got[~pad], want[~pad], f"contiguous random G={groups}")
+
+
+def _random_masked_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        g = int(rng.integers(1, 25))
+        max_m = int(rng.integers(1, 401))
+        mm = rng.integers(0, max_m + 1, size=g)
+        mm[rng.random(g) < 0.15] = 0
+        mm[rng.random(g) < 0.15] = max_m
+        cases.append((g, max_m, 8 * int(rng.integers(1, 160)), 128 * int(rng.integers(1, 17)), mm.tolist(),
+                      int(rng.choice([1, 16, 64, 65, 128, 4096])), int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_masked_cases(8, seed=78))
+def test_masked_random_counts(case):
+    """Random group counts, row bounds, masked_m and expected_m hints: rows below
+    masked_m match the oracle, rows at or past it keep the sentinel."""
+    groups, max_m, n, k, mm, hint, seed = case
+    print(f"masked random G={groups} max_m={max_m} {n}x{k} hint {hint} masked_m={mm}", flush=True)
+    qa, sa, qb, sb, masked_m = _masked_host(groups, max_m, n, k, seed=seed, masked_m=mm)
+    got = _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=hint)
+    rows = np.asarray(mm)
+    valid = np.arange(max_m)[None, :] < rows[:, None]
+    assert np.all(got[~valid] == SENTINEL), "rows at or past masked_m were written"
+    if valid.any():
+        want = ogemm.m_grouped_masked(qa, sa, qb, sb, masked_m)
+        assert_gemm_close(got[valid], want[valid], f"masked random G={groups}")
+
+
 def _masked_host(groups, max_m, n, k, seed, masked_m):
     w = synth.masked(groups, max_m, n, k, seed, expected_m=max_m // 2)
     qa, sa = quant.per_token_cast(w.a.reshape(groups * max_m, k))

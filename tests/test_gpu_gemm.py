@@ -455,3 +455,54 @@ def test_dense_full_size_every_element():
     want = ogemm.gemm_nt(oqa, osa, oqb, osb)
     stats = assert_gemm_close(got, want, f"{m}x{n}x{k} every element")
     print(f"every element within tolerance, rel. Frobenius {stats['fro']:.2e}", flush=True)
+
+
+def test_dense_step_graph_replays_bit_for_bit():
+    """The benchmark's dense step (the 15 LLM-layer GEMMs at full size, the
+    planner's own plans, split-K shapes on their own workspaces) captured once in
+    a HIP graph and replayed three times, with eager calls on the same
+    workspaces in between: every replay gives the eager step's bits."""
+    dev = device()
+    shapes = synth.config1_shapes()
+    probs = []
+    for idx, (m, n, k) in enumerate(shapes):
+        g = torch.Generator(device=dev).manual_seed(synth.seed_for(1, idx))
+        qa = (torch.randint(0, 0x7F, (m, k), dtype=torch.uint8, device=dev, generator=g)
+              | (torch.randint(0, 2, (m, k), dtype=torch.uint8, device=dev, generator=g) << 7))
+        qb = (torch.randint(0, 0x7F, (n, k), dtype=torch.uint8, device=dev, generator=g)
+              | (torch.randint(0, 2, (n, k), dtype=torch.uint8, device=dev, generator=g) << 7))
+        sa = mn_major_scales(m, k // 128)
+        sa.copy_(torch.exp2(torch.rand((m, k // 128), device=dev, generator=g) * 8 - 12))
+        sb = torch.exp2(torch.rand(((n + 127) // 128, k // 128), device=dev, generator=g) * 8 - 12)
+        ws = torch.zeros(max(dg.workspace_size(m, n, k), 16), dtype=torch.uint8, device=dev)
+        probs.append(((qa.view(torch.float8_e4m3fn), sa), (qb.view(torch.float8_e4m3fn), sb), ws))
+
+    def step(outs):
+        for (a, b, ws), d in zip(probs, outs):
+            dg.fp8_gemm_nt(a, b, d, workspace=ws)
+
+    eager = [sentinel_like((a[0].shape[0], b[0].shape[0])) for a, b, _ in probs]
+    step(eager)
+    torch.cuda.synchronize()
+    want = [bits(d) for d in eager]
+    outs = [sentinel_like(d.shape) for d in eager]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    print("dense step: capturing 15 GEMMs", flush=True)
+    with torch.cuda.graph(graph, stream=s):
+        step(outs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for d in outs:
+            d.view(torch.int16).fill_(0x7FC1)
+        print(f"dense step: replay {r}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        for (m, n, k), d, w in zip(shapes, outs, want):
+            assert np.array_equal(bits(d), w), f"replay {r}, {m}x{n}x{k}: differs from the eager step"
+        step(eager)                      # eager calls on the same workspaces between replays
+        torch.cuda.synchronize()
+        for (m, n, k), d, w in zip(shapes, eager, want):
+            assert np.array_equal(bits(d), w), f"eager after replay {r}, {m}x{n}x{k}"
+    del graph

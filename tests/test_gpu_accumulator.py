@@ -28,8 +28,14 @@ each product only within a 14-bit window below the block's largest product
 (products more than 2^13 below it are dropped, each on its own, before they
 are summed), the matrix unit's counterpart of the roughly 14-bit accumulation
 the pages describe.  Promotion after every 128-wide block, which these kernels
-do, confines that loss to one block.  The last case pins the window on the
-hardware through D = C + A.B^T with C = -(largest product).
+do, confines that loss to one block.  test_mfma_block_sum_window pins the window
+on the hardware through D = C + A.B^T with C = -(largest product).
+
+The promotion itself, the MFMA's fp32 add of the block's partial into its
+accumulator input, rounds the partial's excess bits to nearest even but
+truncates the accumulator's bits that a larger partial pushes below the
+result's fp32 grid toward minus infinity (test_mfma_accumulator_input_alignment):
+at most one fp32 ulp per K block, and not sign-symmetric.
 """
 import numpy as np
 import pytest
@@ -210,3 +216,85 @@ def test_mfma_block_sum_window():
         assert got[i, 0] == np.float32(model[i]), (big, smalls, got[i, 0], model[i], exact[i])
     dropped = [i for i in range(m) if model[i] != exact[i]]
     assert dropped, "the window cases must include products below it"
+
+
+
+def _code(p, mant=0):
+    """E4M3 code of (1 + mant/8) * 2^p (normal range)."""
+    return ((p + 7) << 3) | mant
+
+
+def _floor32(x):
+    """The largest float32 not above the float64 x."""
+    f = np.float32(x)
+    return f if float(f) <= x else np.nextafter(f, np.float32(-np.inf))
+
+
+def test_mfma_accumulator_input_alignment():
+    """How the block-scaled MFMA adds a K block's sum S into its fp32 input C
+    (the promotion step), pinned bit for bit with power-of-two scales (no
+    rescale) and one product per K block:
+
+    * S the smaller operand (C = +-2^24 from block 0, S = +-0.75 .. +-3 in
+      block 1): the bits of S below the result's fp32 grid are rounded to
+      nearest even;
+    * C the smaller operand (C = +-(1 + 2^-d) after blocks 0 and 1, then a
+      block of 2^p): C's bits below the result's grid are truncated toward
+      minus infinity, so the result is floor32(2^p + C), one fp32 ulp under
+      the nearest value when C is negative and its low bit falls below the
+      result's grid.
+
+    The fp32 promotion is therefore exact whenever the sum is representable
+    (the tests above) and otherwise off by at most one fp32 ulp per K block.
+    The truncation of C is not sign-symmetric: negating A negates D bit for bit
+    only where no promotion drops bits of C (power-of-two scales or a single K
+    block; see test_gpu_gemm.py's negation test).
+
+    The epilogue's fp32 addend subtracts the exact sum rounded to nearest, so D
+    holds the deviation of the accumulator from it (0 or one fp32 ulp)."""
+    rows = []
+    for s in (1, -1):
+        for (tp, tm) in ((-1, 4), (0, 0), (0, 2), (0, 4), (0, 6), (1, 4)):      # 0.75, 1, 1.25, 1.5, 1.75, 3
+            for ts in (1, -1):
+                rows.append(("S", s, (tp, tm), ts))
+    for d in (23, 20, 16, 12):
+        for p in (0, 4, 8, 12, 16):
+            for s in (1, -1):
+                rows.append(("C", s, d, p))
+    m, n, k = len(rows), 8, 384
+    a = np.zeros((m, k), np.uint8)
+    b = np.zeros((n, k), np.uint8)
+    sfa = np.ones((m, 3), np.float32)
+    c = np.zeros((m, n), np.float32)
+    expect = np.zeros(m)
+    for i, row in enumerate(rows):
+        if row[0] == "S":
+            _, s, (tp, tm), ts = row
+            a[i, 0] = _code(8) | (0x80 if s < 0 else 0)          # 256 * 256 * 2^8 = 2^24 (K position 0)
+            sfa[i, 0] = 2.0 ** 8
+            a[i, 128] = _code(tp, tm) | (0x80 if ts < 0 else 0)  # t * 1
+            x = s * 2.0 ** 24 + ts * (1 + tm / 8) * 2.0 ** tp
+            r = float(np.float32(x))                           # nearest even
+        else:
+            _, s, d, p = row                                     # K positions 1, 129, 257 (B = 1 there)
+            a[i, 1] = _code(0) | (0x80 if s < 0 else 0)          # s * 1
+            a[i, 129] = _code(0) | (0x80 if s < 0 else 0)        # s * 2^-d
+            sfa[i, 1] = 2.0 ** -d
+            a[i, 257] = _code(0)                                 # 2^p
+            sfa[i, 2] = 2.0 ** p
+            x = 2.0 ** p + s * (1 + 2.0 ** -d)
+            r = float(_floor32(x))                             # toward minus infinity
+        c[i] = -np.float32(x)
+        expect[i] = r - float(np.float32(x))
+    b[:, 0] = _code(8)                                           # S rows: K positions 0 and 128
+    b[:, 128] = _code(0)
+    b[:, [1, 129, 257]] = _code(0)
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt((upload_codes(a), upload(sfa)), (upload_codes(b), upload(np.ones((1, 3), np.float32))), d,
+                   c=upload(c), workspace=None)
+    torch.cuda.synchronize()
+    got = (bits(d).astype(np.uint32) << 16).view(np.float32)
+    assert np.all(got == got[:, :1]), "columns differ"
+    bad = [(row, float(got[i, 0]), expect[i]) for i, row in enumerate(rows) if float(got[i, 0]) != expect[i]]
+    assert not bad, bad[:6]
+    assert any(expect[i] != 0 for i, row in enumerate(rows) if row[0] == "C"), "no C truncation among the cases"

@@ -143,6 +143,36 @@ def test_power_of_two_scale_linearity_bit_exact():
     assert np.array_equal(f(down), f(base) * np.float32(0.25))
 
 
+@pytest.mark.parametrize("m,n,k,ue8m0", [(300, 520, 640, True), (64, 2112, 1536, True), (4096, 2880, 640, True),
+                                         (300, 520, 128, False), (4096, 2880, 128, False)])
+def test_negation_and_zero_rows_bit_exact(m, n, k, ue8m0):
+    """Sign symmetry of the whole path, bit for bit, under the planner's own plan
+    (128x64 tiles, split K and 256x256 tiles among the shapes): negating A (or B)
+    negates every nonzero output, a zero stays a zero, and A rows of zero codes
+    give rows of +0.  This holds wherever no K block's promotion drops low bits
+    of the running fp32 sum: over a single K block, and on these inputs with
+    power-of-two scales, whose running sums keep few bits (they add up products
+    the MFMA has already cut to its 14-bit window, with no rescale).  With fp32
+    scales over several K blocks the rescaled running sum carries all 24 bits,
+    the MFMA truncates the ones a larger block sum pushes below the result's
+    grid toward minus infinity (pinned by test_gpu_accumulator.py's
+    test_mfma_accumulator_input_alignment), and a few outputs in a million then
+    differ from the exact negation by a bf16 ulp or two."""
+    print(f"negation {m}x{n}x{k} ue8m0={ue8m0} plan {dg.tile_config(m, n, k)}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + n + k, ue8m0=ue8m0)
+    zero_rows = sorted({0, min(17, m - 1), m - 1})
+    qa[zero_rows] = 0
+    base = _gpu_dense(qa, sa, qb, sb)
+    neg_a = _gpu_dense(qa ^ np.uint8(0x80), sa, qb, sb)
+    neg_b = _gpu_dense(qa, sa, qb ^ np.uint8(0x80), sb)
+    zero = (base & 0x7FFF) == 0
+    assert np.all(base[zero_rows] == 0), "rows of zero codes are not +0"
+    for got, what in ((neg_a, "-A"), (neg_b, "-B")):
+        assert np.array_equal(got[~zero], base[~zero] ^ np.uint16(0x8000)), f"{what}: not the negation"
+        assert np.all((got[zero] & 0x7FFF) == 0), f"{what}: a zero output is not a zero"
+    assert_gemm_close(base, ogemm.gemm_nt(qa, sa, qb, sb), f"negation base {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 520, 4096), (1, 8, 128), (256, 512, 1024)])
 def test_accumulate_parity(m, n, k):
     # D = RNE_bf16(C + A.B^T); (64, 520, 4096) takes the split-K path, where the

@@ -404,9 +404,11 @@ def sample_blocks_and_cols(rng, n, blocks, per_block):
     return chosen, np.array(cols)
 
 
-def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=False):
+def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=False, min_exact=None):
     """Oracle re-quantization of the sampled pieces (bit-exact vs the GPU casts)
-    and the sampled GEMM outputs (tolerance)."""
+    and the sampled GEMM outputs (tolerance).  min_exact: least fraction of the
+    sampled outputs that must equal the oracle's bf16 result bit for bit (at
+    most 1% may then be more than one bf16 ulp away)."""
     n = b32.shape[0]
     a_rows32 = a32[torch.as_tensor(rows, device=a32.device)].cpu().numpy()
     oqa, osa = quant.per_token_cast(a_rows32, ue8m0)
@@ -428,7 +430,15 @@ def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=F
     ri = torch.as_tensor(rows, device=d.device)
     ci = torch.as_tensor(cols, device=d.device)
     got = bits(d[ri][:, ci])
-    return assert_gemm_close(got, want, what)
+    stats = assert_gemm_close(got, want, what)
+    if min_exact is not None:
+        g, w = got.astype(np.int32), want.astype(np.int32)
+        ulps = np.where((g & 0x8000) == (w & 0x8000), np.abs((g & 0x7FFF) - (w & 0x7FFF)), 1 << 16)
+        exact = float(np.mean(ulps == 0))
+        assert exact >= min_exact, f"{what}: only {exact:.4f} of the sampled outputs equal the oracle's bits"
+        assert float(np.mean(ulps > 1)) <= 0.01, f"{what}: {float(np.mean(ulps > 1)):.4f} are over one bf16 ulp away"
+        stats["exact"] = exact
+    return stats
 
 
 def mn_major_scales(rows, kblocks):
@@ -454,7 +464,9 @@ def test_dense_full_size_sampled(idx):
     rng = np.random.default_rng(seed)
     rows = sample_rows(rng, m, 24)
     blocks, cols = sample_blocks_and_cols(rng, n, 3, 12)
-    check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, f"{m}x{n}x{k}")
+    # most outputs are the exactly rounded result: about 98.8% on these shapes (the
+    # rest one bf16 ulp off, or near zero after cancellation)
+    check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, f"{m}x{n}x{k}", min_exact=0.95)
     # every output element was written (no sentinel left, nothing non-finite)
     assert bool(torch.isfinite(d.float()).all())
 

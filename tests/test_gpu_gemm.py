@@ -406,9 +406,10 @@ def sample_blocks_and_cols(rng, n, blocks, per_block):
 
 def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=False, min_exact=None):
     """Oracle re-quantization of the sampled pieces (bit-exact vs the GPU casts)
-    and the sampled GEMM outputs (tolerance).  min_exact: least fraction of the
-    sampled outputs that must equal the oracle's bf16 result bit for bit (at
-    most 1% may then be more than one bf16 ulp away)."""
+    and the sampled GEMM outputs (tolerance).  Returns the tolerance statistics
+    and the counts of sampled outputs that equal the oracle's bf16 result bit for
+    bit (``n_exact``) or lie more than one bf16 ulp from it (``n_far``), out of
+    ``n``; with ``min_exact`` those rates are asserted here (assert_exact_rate)."""
     n = b32.shape[0]
     a_rows32 = a32[torch.as_tensor(rows, device=a32.device)].cpu().numpy()
     oqa, osa = quant.per_token_cast(a_rows32, ue8m0)
@@ -431,14 +432,24 @@ def check_sampled(a32, qa, sa, b32, qb, sb, d, rows, blocks, cols, what, ue8m0=F
     ci = torch.as_tensor(cols, device=d.device)
     got = bits(d[ri][:, ci])
     stats = assert_gemm_close(got, want, what)
+    g, w = got.astype(np.int32), want.astype(np.int32)
+    # distance in bf16 ulps between outputs of equal sign; a sign flip counts as far
+    ulps = np.where((g & 0x8000) == (w & 0x8000), np.abs((g & 0x7FFF) - (w & 0x7FFF)), 1 << 16)
+    stats.update(n=int(ulps.size), n_exact=int(np.sum(ulps == 0)), n_far=int(np.sum(ulps > 1)))
     if min_exact is not None:
-        g, w = got.astype(np.int32), want.astype(np.int32)
-        ulps = np.where((g & 0x8000) == (w & 0x8000), np.abs((g & 0x7FFF) - (w & 0x7FFF)), 1 << 16)
-        exact = float(np.mean(ulps == 0))
-        assert exact >= min_exact, f"{what}: only {exact:.4f} of the sampled outputs equal the oracle's bits"
-        assert float(np.mean(ulps > 1)) <= 0.01, f"{what}: {float(np.mean(ulps > 1)):.4f} are over one bf16 ulp away"
-        stats["exact"] = exact
+        assert_exact_rate([stats], min_exact, what)
     return stats
+
+
+def assert_exact_rate(stats, min_exact, what):
+    """At least ``min_exact`` of the sampled outputs (summed over check_sampled
+    results) equal the oracle's exactly rounded bf16 result bit for bit, and at
+    most 1% lie more than one bf16 ulp away from it."""
+    n = sum(s["n"] for s in stats)
+    exact = sum(s["n_exact"] for s in stats) / n
+    far = sum(s["n_far"] for s in stats) / n
+    assert exact >= min_exact, f"{what}: only {exact:.4f} of {n} sampled outputs equal the oracle's bits"
+    assert far <= 0.01, f"{what}: {far:.4f} of {n} sampled outputs are over one bf16 ulp away"
 
 
 def mn_major_scales(rows, kblocks):

@@ -113,6 +113,52 @@ def test_dense_long_k(m, n, k):
     assert_gemm_close(bits(d), want, f"{m}x{n}x{k} unsplit")
 
 
+# plans: 128x128 tiles, 64x64 tiles, 256x256 tiles (A side, B side), 64x64 tiles split 4 ways over K
+@pytest.mark.parametrize("m,n,k,side", [(4095, 1024, 512, "a"), (64, 4088, 512, "b"), (1000, 4088, 256, "b"),
+                                        (4095, 4096, 2048, "a"), (4088, 4088, 1024, "b"), (64, 4088, 7168, "b")])
+def test_dense_operand_offsets_near_the_32bit_limit(m, n, k, side):
+    """The kernels address operand rows with 32-bit per-lane byte offsets (rows x
+    leading dimension < 2^32).  With rows 1 MiB apart, the last rows of A (or B)
+    lie just under 4 GiB from the first: every output still matches the oracle,
+    and a problem one row (A) or eight rows (B) larger is rejected before any
+    launch, leaving D untouched."""
+    ld = 1 << 20
+    rows = m if side == "a" else n
+    more = 1 if side == "a" else 8
+    assert (rows - 1) * ld + k < 2 ** 32 <= (rows + more) * ld
+    print(f"dense {m}x{n}x{k}, {side} rows {ld} bytes apart, plan {dg.tile_config(m, n, k)}", flush=True)
+    qa, sa, qb, sb = _host_problem(m, n, k, seed=m + n + k)
+    dev = device()
+    buf = torch.zeros((rows + more - 1) * ld + k, dtype=torch.uint8, device=dev)
+
+    def spread(r, q=None):
+        v = buf.as_strided((r, k), (ld, 1))
+        if q is not None:
+            v.copy_(torch.from_numpy(q).to(dev))
+        return v.view(torch.float8_e4m3fn)
+
+    if side == "a":
+        a, b = (spread(m, qa), upload(sa)), (upload_codes(qb), upload(sb))
+    else:
+        a, b = (upload_codes(qa), upload(sa)), (spread(n, qb), upload(sb))
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, b, d)
+    torch.cuda.synchronize()
+    assert_gemm_close(bits(d), ogemm.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k} {side} at the offset limit")
+    # one row more no longer fits the 32-bit offsets
+    if side == "a":
+        a = (spread(m + more), upload(np.ones((m + more, k // 128), np.float32)))
+        d = sentinel_like((m + more, n))
+    else:
+        b = (spread(n + more), upload(np.ones(((n + more + 127) // 128, k // 128), np.float32)))
+        d = sentinel_like((m, n + more))
+    with pytest.raises(dg.DgError) as err:
+        dg.fp8_gemm_nt(a, b, d)
+    assert err.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()
+    assert bool((d.view(torch.int16) == 0x7FC1).all()), "a rejected call wrote D"
+
+
 def test_config0_workload():
     w = synth.config0()
     qa, sa = quant.per_token_cast(w.a)

@@ -550,6 +550,77 @@ def _gpu_masked(qa, sa, qb, sb, masked_m, expected_m=64):
     return bits(d)
 
 
+def test_grouped_offsets_near_the_32bit_limit():
+    """One group's A rows are addressed with 32-bit per-lane byte offsets (rows x
+    leading dimension < 2^32); groups are 64-bit apart.  Contiguous: 4096 rows
+    1 MiB - 16 bytes apart, the last just under 4 GiB from the first.  Masked:
+    two groups of 4095 rows 1 MiB apart, the second group 4 GiB after the first.
+    Both match the oracle on every valid row; one M tile (contiguous) or one row
+    per group (masked) more is rejected before any launch, leaving D untouched."""
+    dev = device()
+    n, k = 256, 512
+    b32 = np.stack([synth.dense(1, n, k, 90 + g).b for g in range(4)])
+    qb, sb = _quant_groups(b32)
+    b = (upload_codes(qb), upload(sb))
+
+    # contiguous: segments of 1000, 1500, 0 and 1450 tokens, each padded to 128 rows
+    m_indices = np.concatenate([np.r_[np.full(c, g), np.full(-c % 128, -1)] for g, c in
+                                enumerate([1000, 1500, 0, 1450])]).astype(np.int32)
+    m_total, lda = m_indices.size, (1 << 20) - 16
+    assert m_total == 4096 and (m_total - 1) * lda + k < 2 ** 32 <= (m_total + 128) * lda
+    print(f"contiguous {m_total}x{n}x{k}, A rows {lda} bytes apart", flush=True)
+    a32 = synth.dense(m_total, 8, k, 91).a
+    a32[m_indices < 0] = 0.0
+    qa, sa = quant.per_token_cast(a32)
+    buf = torch.zeros((m_total + 127) * lda + k, dtype=torch.uint8, device=dev)
+    a_rows = buf.as_strided((m_total, k), (lda, 1))
+    a_rows.copy_(torch.from_numpy(qa).to(dev))
+    d = sentinel_like((m_total, n))
+    dg.m_grouped_fp8_gemm_nt_contiguous((a_rows.view(torch.float8_e4m3fn), upload(sa)), b, d, upload(m_indices))
+    torch.cuda.synchronize()
+    got, valid = bits(d), m_indices >= 0
+    assert np.all(got[~valid] == SENTINEL), "padding rows were written"
+    want = ogemm.m_grouped_contiguous(qa, sa, qb, sb, m_indices)
+    assert_gemm_close(got[valid], want[valid], "contiguous at the offset limit")
+    more = np.r_[m_indices, np.full(128, 1, np.int32)]
+    d = sentinel_like((m_total + 128, n))
+    with pytest.raises(dg.DgError) as err:
+        dg.m_grouped_fp8_gemm_nt_contiguous((buf.as_strided((m_total + 128, k), (lda, 1)).view(torch.float8_e4m3fn),
+                                             upload(np.ones((m_total + 128, k // 128), np.float32))), b, d,
+                                            upload(more))
+    assert err.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    del buf, a_rows
+
+    # masked: group stride 2^32 bytes, rows 2^20 bytes apart
+    g, max_m, lda, gs = 2, 4095, 1 << 20, 1 << 32
+    assert (max_m - 1) * lda + k < 2 ** 32 <= (max_m + 1) * lda
+    print(f"masked {g}x{max_m}x{n}x{k}, A rows {lda} and groups {gs} bytes apart", flush=True)
+    masked_m = np.array([4095, 2500], np.int32)
+    a32 = synth.dense(g * max_m, 8, k, 92).a.reshape(g, max_m, k)
+    qa, sa = quant.per_token_cast(a32.reshape(-1, k))
+    qa, sa = qa.reshape(g, max_m, k), sa.reshape(g, max_m, k // 128)
+    buf = torch.zeros((g - 1) * gs + max_m * lda + k, dtype=torch.uint8, device=dev)
+    a_rows = buf.as_strided((g, max_m, k), (gs, lda, 1))
+    a_rows.copy_(torch.from_numpy(qa).to(dev))
+    d = sentinel_like((g, max_m, n))
+    dg.m_grouped_fp8_gemm_nt_masked((a_rows.view(torch.float8_e4m3fn), upload(sa)), (b[0][:g], b[1][:g]), d,
+                                    upload(masked_m), 2048)
+    torch.cuda.synchronize()
+    got = bits(d)
+    want = ogemm.m_grouped_masked(qa, sa, qb[:g], sb[:g], masked_m)
+    for gg, c in enumerate(masked_m):
+        assert np.all(got[gg, c:] == SENTINEL), f"group {gg}: rows beyond masked_m written"
+        assert_gemm_close(got[gg, :c], want[gg, :c], f"masked group {gg} at the offset limit")
+    d = sentinel_like((g, max_m + 1, n))
+    with pytest.raises(dg.DgError) as err:
+        dg.m_grouped_fp8_gemm_nt_masked((buf.as_strided((g, max_m + 1, k), (gs, lda, 1)).view(torch.float8_e4m3fn),
+                                         upload(np.ones((g, max_m + 1, k // 128), np.float32))),
+                                        (b[0][:g], b[1][:g]), d, upload(masked_m), 2048)
+    assert err.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()
+    assert bool((d.view(torch.int16) == SENTINEL).all()), "a rejected call wrote D"
+
+
 def test_masked_parity_small_with_edge_counts():
     mm = [0, 1, 127, 128, 129, 200, 300]                 # 300 > max_m clamps to 200
     qa, sa, qb, sb, masked_m = _masked_host(7, 200, 264, 384, seed=21, masked_m=mm)

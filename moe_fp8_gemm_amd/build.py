@@ -44,10 +44,11 @@ def _flags():
             "-Wno-unused-command-line-argument"]
 
 
-# Per-source extra flags.  The GEMM promotes every MFMA result with VALU FMAs, so
-# MFMA results must land in VGPRs: force the VGPR-destination MFMA form (LLVM
+# Per-source extra flags.  With fp32 scales the GEMM multiplies its MFMA
+# accumulators on the VALU between K blocks (the scale mantissa), so the
+# accumulators must live in VGPRs: force the VGPR-destination MFMA form (LLVM
 # otherwise picks the AGPR form for kernels allowed more than 256 VGPRs, and each
-# result then needs extra v_accvgpr_read moves).
+# rescale then needs v_accvgpr_read/write moves).
 EXTRA_FLAGS = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

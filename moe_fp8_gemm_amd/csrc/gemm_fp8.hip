@@ -719,8 +719,25 @@ gemm_kernel(GemmParams p) {
       }
     }
   };
+  // First tile of round r (tiles r*grid .. r*grid + grid - 1).  A round that
+  // the dense tiles fill only in part is spread evenly over the 8 XCDs (each
+  // takes a contiguous run of about a eighth of it) instead of filling the
+  // first XCDs and leaving the others idle; the full rounds keep the
+  // contiguous per-XCD runs of remap_for_xcd.  Only the tile-to-workgroup map
+  // changes: every tile is still run once, by one workgroup.
+  auto round_start = [&](int r) -> int {
+    const int grid = (int)gridDim.x, t0 = r * grid;
+    if (V == kDense && grid % 8 == 0 && t0 < num_tiles && num_tiles - t0 < grid) {
+      const int rem = num_tiles - t0, q = rem >> 3, extra = rem & 7;
+      const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+      const int cnt = q + (x < extra ? 1 : 0);
+      return j < cnt ? t0 + x * q + min(x, extra) + j : num_tiles;
+    }
+    return t0 < num_tiles ? t0 + remap_for_xcd((int)blockIdx.x, grid) : num_tiles;
+  };
+  int rnd = 0;
   Tile cur;
-  int tile = next_tile(remap_for_xcd(blockIdx.x, gridDim.x), cur);
+  int tile = next_tile(round_start(0), cur);
   if (tile < num_tiles) prologue(cur);
   while (tile < num_tiles) {
     f32x4 acc[C::MS][C::NS];
@@ -760,7 +777,7 @@ gemm_kernel(GemmParams p) {
         for (int j = 0; j < C::NS; ++j) acc[ms][j] *= mant[ms];
     }
     Tile nxt;
-    const int ntile = next_tile(tile + gridDim.x, nxt);
+    const int ntile = next_tile(V == kDense ? round_start(++rnd) : tile + (int)gridDim.x, nxt);
     if (kSplit && splits > 1) {
       // Publish this unit's partial tile, count arrivals; the last unit of the
       // output tile adds all partials in split order (deterministic whatever the
